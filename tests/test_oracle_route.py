@@ -1,0 +1,122 @@
+"""Pins for the oracle's router logits and top-k routing (CPU only)."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import route as RT
+from oracle.formats import bf16_to_f64
+
+
+def _bf16_bits(x):
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_logits_match_exact_sums():
+    rng = np.random.default_rng(11)
+    R, E, h = 3, 24, 512
+    x = _bf16_bits(rng.standard_normal((R, h)))
+    w = (rng.standard_normal((E, h)) / math.sqrt(h)).astype(np.float32)
+    L = RT.router_logits(x, w)
+    xf = bf16_to_f64(x)
+    mism = 0
+    for r in range(R):
+        for e in range(E):
+            exact = math.fsum(float(a) * float(b) for a, b in zip(xf[r], w[e].astype(np.float64)))
+            ref = np.float32(exact)
+            if L[r, e] != ref:
+                mism += 1
+                assert abs(float(L[r, e]) - float(ref)) <= np.spacing(np.float32(abs(ref))), (r, e)
+    assert mism <= 1
+
+
+def test_logits_one_hot_input():
+    E, h = 8, 64
+    w = np.random.default_rng(2).standard_normal((E, h)).astype(np.float32)
+    x = np.zeros((1, h), np.uint16)
+    x[0, 17] = 0x3F80  # bf16 1.0
+    assert np.array_equal(RT.router_logits(x, w)[0], w[:, 17])
+
+
+def test_select_matches_stable_argsort_with_ties():
+    rng = np.random.default_rng(12)
+    for trial in range(200):
+        E = int(rng.integers(1, 40))
+        k = int(rng.integers(1, E + 1))
+        keys = rng.integers(-3, 4, size=E).astype(np.float32)  # many exact ties
+        ref = np.argsort(-keys.astype(np.float64), kind="stable")[:k].tolist()
+        assert RT.select_topk(keys, k) == ref
+
+
+def test_zero_router_softmax():
+    E, k = 16, 4
+    L = np.zeros((2, E), np.float32)
+    ids, w = RT.topk_softmax(L, k, True)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 2
+    assert np.all(w == np.float32(0.25))
+    ids, w = RT.topk_softmax(L, k, False)
+    assert np.all(w == np.float32(1.0 / 16))
+
+
+def test_zero_router_sigmoid_selects_by_bias():
+    E, k, rsf = 32, 5, 2.5
+    bias = np.random.default_rng(4).uniform(-0.1, 0.1, E).astype(np.float32)
+    L = np.zeros((1, E), np.float32)
+    ids, w = RT.topk_sigmoid_bias(L, bias, k, True, rsf)
+    keys = (np.float32(0.5) + bias).astype(np.float32)
+    assert ids[0].tolist() == np.argsort(-keys.astype(np.float64), kind="stable")[:k].tolist()
+    assert np.all(w == np.float32(rsf / k))
+    ids, w = RT.topk_sigmoid_bias(L, bias, k, False, rsf)
+    assert np.all(w == np.float32(0.5 * rsf))
+
+
+def test_topk_equals_all_experts():
+    rng = np.random.default_rng(13)
+    L = rng.standard_normal((3, 8)).astype(np.float32)
+    ids, w = RT.topk_softmax(L, 8, True)
+    for r in range(3):
+        assert sorted(ids[r].tolist()) == list(range(8))
+        assert abs(float(w[r].astype(np.float64).sum()) - 1.0) < 1e-6
+
+
+def test_softmax_norm_is_softmax_over_selected():
+    rng = np.random.default_rng(14)
+    L = (rng.standard_normal((6, 64)) * 3).astype(np.float32)
+    ids, w = RT.topk_softmax(L, 8, True)
+    for r in range(6):
+        sel = L[r, ids[r]].astype(np.float64)
+        ref = np.exp(sel - sel.max())
+        ref /= ref.sum()
+        np.testing.assert_allclose(w[r].astype(np.float64), ref, rtol=1e-7, atol=0)
+        assert np.all(np.diff(sel) <= 0)  # descending logits
+
+
+def test_weights_sum_invariants():
+    rng = np.random.default_rng(15)
+    L = rng.standard_normal((8, 256)).astype(np.float32)
+    bias = rng.uniform(-0.1, 0.1, 256).astype(np.float32)
+    _, w = RT.topk_softmax(L, 8, True)
+    assert np.all(np.abs(w.astype(np.float64).sum(1) - 1.0) < 1e-6)
+    _, w = RT.topk_sigmoid_bias(L, bias, 8, True, 2.5)
+    assert np.all(np.abs(w.astype(np.float64).sum(1) / 2.5 - 1.0) < 1e-6)
+
+
+def test_sigmoid_weights_are_unbiased_scores():
+    # Weights use sigmoid(L) without the bias: a large bias changes the
+    # selection but not the weight of a selected expert.
+    L = np.array([[0.0, 1.0, -1.0, 2.0]], np.float32)
+    bias = np.array([5.0, 0.0, 0.0, 0.0], np.float32)
+    ids, w = RT.topk_sigmoid_bias(L, bias, 2, False, 1.0)
+    assert ids[0].tolist() == [0, 3]
+    assert w[0, 0] == np.float32(0.5)
+    assert w[0, 1] == np.float32(1.0 / (1.0 + math.exp(-2.0)))
+
+
+def test_sigmoid_keys_fp32_add():
+    L = np.array([[0.25, -3.0]], np.float32)
+    bias = np.array([0.01, -0.02], np.float32)
+    k = RT.sigmoid_keys(L, bias)
+    s32 = np.float32(1.0 / (1.0 + math.exp(-0.25)))
+    assert k[0, 0] == np.float32(s32 + np.float32(0.01))

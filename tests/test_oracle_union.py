@@ -1,0 +1,67 @@
+"""Pins for the oracle's expert union (CPU only)."""
+
+import itertools
+
+import numpy as np
+
+from oracle.union import expert_union
+
+
+def _check(ids):
+    ids = np.asarray(ids)
+    R, k = ids.shape
+    flat = ids.reshape(-1).tolist()
+    union_ids, U, s2u, mask = expert_union(ids)
+    ref = list(dict.fromkeys(flat))             # insertion-ordered dedup
+    assert union_ids.tolist() == ref
+    assert U == len(set(flat))
+    assert k <= U <= min(k * R, max(flat) + 1)
+    for t, e in enumerate(flat):
+        assert union_ids[s2u[t]] == e
+    for u, e in enumerate(ref):
+        rows = {t // k for t, v in enumerate(flat) if v == e}
+        assert int(mask[u]) == sum(1 << r for r in rows)
+
+
+def test_union_exhaustive_tiny():
+    n = 0
+    for E in range(1, 6):
+        for k in range(1, min(E, 3) + 1):
+            row_choices = list(itertools.permutations(range(E), k))
+            for R in range(1, 4):
+                if len(row_choices) ** R > 4000:
+                    combos = [tuple(row_choices[i] for i in np.random.default_rng(E * 100 + k * 10 + R)
+                                    .integers(0, len(row_choices), R)) for _ in range(400)]
+                else:
+                    combos = itertools.product(row_choices, repeat=R)
+                for rows in combos:
+                    _check(np.array(rows))
+                    n += 1
+    assert n > 5000
+
+
+def test_union_extremes():
+    k = 8
+    # all rows identical: U = k
+    ids = np.tile(np.arange(k), (8, 1))
+    u, U, s2u, mask = expert_union(ids)
+    assert U == k and np.all(mask == 0xFF) and s2u.tolist() == list(range(k)) * 8
+    # all distinct: U = 64 = k * rows (the one-block maximum)
+    ids = np.arange(64).reshape(8, 8)
+    u, U, s2u, mask = expert_union(ids)
+    assert U == 64 and s2u.tolist() == list(range(64))
+    assert [int(m) for m in mask] == [1 << (t // 8) for t in range(64)]
+    # single row: union is the row itself, in slot order
+    u, U, _, _ = expert_union(np.array([[5, 3, 9]]))
+    assert u.tolist() == [5, 3, 9]
+
+
+def test_union_random_large():
+    rng = np.random.default_rng(21)
+    for _ in range(300):
+        E = int(rng.integers(8, 300))
+        k = int(rng.integers(1, 9))
+        R = int(rng.integers(1, 64 // k + 1))
+        R = min(R, 8)
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(R)])
+        _check(ids)

@@ -1,0 +1,78 @@
+"""The seeded input generator: reproducibility, encodings, distributions (CPU only)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+
+def test_e4m3_encoder_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.abs(rng.standard_normal(200000).astype(np.float32)) * np.float32(0.05)
+    # exact midpoints between neighbouring E4M3 values (ties to even) and subnormals
+    vals = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, vals.astype(np.float32), mids, np.float32([1e-6, 2 ** -10, 447.9, 448.0])])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(synth.f32_to_e4m3fn_bytes(x), ref)
+
+
+def test_bf16_encoder_matches_torch():
+    x = np.random.default_rng(1).standard_normal(100000).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(synth.f32_to_bf16_bits(x), ref)
+
+
+def test_reproducible_and_independent_substreams():
+    s = synth.CONFIGS["c1_e64_decode"]
+    a = synth.expert_tensor(s, 3, 1)
+    b = synth.expert_tensor(s, 3, 1)
+    c = synth.expert_tensor(s, 4, 1)
+    assert np.array_equal(a.packed, b.packed) and np.array_equal(a.scales, b.scales)
+    assert not np.array_equal(a.packed, c.packed)
+    assert a.packed.shape == (768, 1024) and a.scales.shape == (768, 128)
+    d = synth.expert_tensor(s, 3, 2)
+    assert d.packed.shape == (2048, 384) and d.scales.shape == (2048, 48)
+
+
+def test_activation_prefix_does_not_depend_on_rows():
+    s = synth.CONFIGS["c4_e256_prefill8"]
+    x8 = synth.activations(s, 5, rows=8)
+    for r in range(1, 8):
+        assert np.array_equal(synth.activations(s, 5, rows=r), x8[:r])
+
+
+def test_correlated_rows():
+    s = synth.CONFIGS["c2_e128_verify2"]
+    x = synth.activations(s, 0).astype(np.uint32) << 16
+    xf = x.view(np.float32).astype(np.float64)
+    c = np.corrcoef(xf[0], xf[1])[0, 1]
+    assert abs(c - 0.8) < 0.03
+
+
+def test_distributions():
+    s = synth.CONFIGS["c1_e64_decode"]
+    t = synth.expert_tensor(s, 0, 0)
+    lo, hi = t.packed & 15, t.packed >> 4
+    counts = np.bincount(np.concatenate([lo.ravel(), hi.ravel()]), minlength=16)
+    assert counts.min() > 0.95 * counts.mean() and counts.max() < 1.05 * counts.mean()
+    sv = torch.from_numpy(t.scales.reshape(-1)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert abs(sv.mean() - 0.05 * np.sqrt(2 / np.pi)) < 2e-3  # E|N(0,1)| * 0.05
+    w = synth.router_weight(s)
+    assert abs(w.std() * np.sqrt(s.hidden) - 1.0) < 0.02
+    b = synth.correction_bias(synth.CONFIGS["c2_e128_verify2"])
+    assert b.min() >= -0.1 and b.max() <= 0.1
+
+
+@pytest.mark.slow
+def test_c3_mean_union_near_pages_k4_curve():
+    # Statistical property of the workload (not a parity pin): the mean union
+    # over 200 steps stays near the 23.35 the pages report at K = 4.
+    import importlib.util, os
+    spec = importlib.util.spec_from_file_location(
+        "tune", os.path.join(os.path.dirname(__file__), "golden", "tune_c3_row_corr.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    m, _ = mod.mean_union(synth.CONFIGS["c3_e256_verify4"], steps=200)
+    assert abs(m - 23.35) < 0.6
