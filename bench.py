@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE decode/verify layer on one MI355X.
+
+One step = one ``moe_forward`` (router -> top-k -> union -> gate/up sweep ->
+down sweep -> weighted sum + shared blend) over one batch of rows, inputs
+resident in HBM.  Workload: the 256-expert shape (h=6144, E=256, top_k=8,
+I=Is=2048, sigmoid + correction bias, routed_scaling_factor 2.5, NVFP4
+experts), rows=8 independent N(0,1) rows.  Steps cycle over 16 seeded inputs
+(so unions differ) and over several device copies of the layer (so no step
+finds another step's weights in the 256 MB Infinity Cache).
+
+Prints one JSON line: value = achieved HBM GB/s from algorithmic bytes (each
+step's own union size) over the timed wall time of K steps; per-stage HIP
+events recorded on the launch stream inside the same timed region give the
+dominant kernel's roofline figure.  Also reports the rows=1..8 sweep and the
+CPU oracle timed on a bounded sample (a reference point, not the target).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-MoE layer µs/step + achieved HBM GB/s (% peak), rows=1..8, NVFP4"
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = "c4_e256_prefill8"
+N_INPUTS = 16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_bytes(n: int, k: int) -> int:
+    return n * k // 2 + n * k // 16 + 4
+
+
+def step_bytes(shape, rows: int, U: int) -> dict:
+    """Algorithmic HBM bytes of one step, split by stage."""
+    h, E, k, I, Is = shape.hidden, shape.num_experts, shape.top_k, shape.moe_inter, shape.shared_inter
+    pairs = rows * k
+    nkc = (h + 2047) // 2048
+    router = 4 * E * h + 4 * h + 2 * rows * h + 8 * nkc * rows * (E + 1)
+    topk = 8 * nkc * rows * (E + 1) + (4 * E if shape.route_kind == 1 else 0) + 8 * pairs
+    gateup = 2 * U * expert_bytes(I, h) + 2 * expert_bytes(Is, h) + 2 * rows * h + 2 * (pairs * I + rows * Is)
+    down = U * expert_bytes(h, I) + expert_bytes(h, Is) + 2 * (pairs * I + rows * Is) + 4 * (pairs + rows) * h
+    blend = 4 * (pairs + rows) * h + 2 * rows * h + 8 * pairs
+    # whole layer: weights + router + bias + gate vector + x in + out
+    layer = (U * 3 * expert_bytes(I, h) + 3 * expert_bytes(Is, h) + 4 * E * h
+             + (4 * E if shape.route_kind == 1 else 0) + 4 * h + 4 * rows * h)
+    return dict(layer=layer, router_gemv=router, topk_union=topk, gate_up_sweep=gateup, down_sweep=down,
+                blend=blend)
+
+
+def build_layers(shape, n_layers: int):
+    import torch
+    import mixture_experts_decode_gate_amd as moe
+    from mixture_experts_decode_gate_amd.device import DeviceLayer
+    import synth
+    t0 = time.time()
+    w = synth.layer_weights(shape, materialise=True, threads=16)
+    log(f"[bench] generated {shape.name} weights in {time.time() - t0:.1f}s")
+    cfg = moe.MoeConfig.from_shape(shape)
+    base = DeviceLayer(cfg, w.router_w, w.bias, w.shared_gate_vec, w.shared, w.expert)
+    w._experts.clear()
+    layers = [base] + [base.clone() for _ in range(n_layers - 1)]
+    torch.cuda.synchronize()
+    log(f"[bench] {n_layers} device copies of {base.nbytes() / 1e9:.2f} GB ready after {time.time() - t0:.1f}s")
+    return cfg, layers
+
+
+def union_sizes(cfg, layer, xs, ws):
+    import torch
+    import mixture_experts_decode_gate_amd as moe
+    L = moe.moe_workspace_layout(cfg)
+    out = torch.empty_like(xs[0])
+    us = []
+    for x in xs:
+        moe.moe_forward(cfg, layer.weights, x, out, ws)
+        torch.cuda.synchronize()
+        us.append(int(ws[L.union_count:L.union_count + 4].cpu().numpy().view(np.int32)[0]))
+    return us
+
+
+def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, with_stage_events=True):
+    import torch
+    import mixture_experts_decode_gate_amd as moe
+    from mixture_experts_decode_gate_amd.hip_events import HipEvent
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+    out = torch.empty_like(xs[0])
+    nst = moe.moe_num_stages()
+    for i in range(warmup):
+        moe.moe_forward(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], out, ws)
+    events = [[HipEvent() for _ in range(nst + 1)] for _ in range(steps)] if with_stage_events else None
+    start, end = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(sh)
+    for i in range(steps):
+        lay, xi = layers[i % len(layers)], i % len(xs)
+        if with_stage_events:
+            moe.moe_forward_timed(cfg, lay.weights, xs[xi], out, ws, events[i])
+        else:
+            moe.moe_forward(cfg, lay.weights, xs[xi], out, ws)
+    end.record(sh)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_ms(end)
+    sbytes = [step_bytes(shape, rows, us[i % len(xs)]) for i in range(steps)]
+    res = dict(total_ms=total_ms, host_wall_ms=wall * 1e3, us_per_step=total_ms * 1e3 / steps,
+               layer_bytes=sum(b["layer"] for b in sbytes),
+               mean_union=float(np.mean([us[i % len(xs)] for i in range(steps)])))
+    res["gbps"] = res["layer_bytes"] / (total_ms * 1e-3) / 1e9
+    if with_stage_events:
+        names = moe.moe_stage_names()
+        stage = {}
+        for s, name in enumerate(names):
+            d = [events[i][s].elapsed_ms(events[i][s + 1]) for i in range(steps)]
+            b = sum(sb[name] for sb in sbytes)
+            stage[name] = dict(avg_us=float(np.mean(d)) * 1e3, gbps=b / (sum(d) * 1e-3) / 1e9,
+                               bytes_per_launch=b / steps)
+        res["stages"] = stage
+    return res
+
+
+def copy_reference(nbytes=2 << 30, reps=10):
+    """Achieved bandwidth of a plain device copy (read + write), for context."""
+    import torch
+    from mixture_experts_decode_gate_amd.hip_events import HipEvent
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    e0, e1 = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    e0.record(sh)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(sh)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_ms(e1) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9, ms
+
+
+def cpu_baseline(shape, rows_sample=(0, 1), step=0):
+    """The oracle as it stands, on a bounded sample of the workload: the rows in
+    ``rows_sample`` of one step (routing of all rows, expert FFNs and output for
+    the sampled rows).  Rate = the sample's algorithmic bytes / oracle time."""
+    import synth
+    from oracle.layer import moe_layer_from
+    from oracle.route import route
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    w = synth.layer_weights(shape)
+    x = synth.activations(shape, step)
+    _, ids, _ = route(x, w.router_w, w.bias, shape.route_kind, shape.top_k, shape.norm_topk_prob,
+                      shape.routed_scaling_factor)
+    need = sorted(set(int(e) for r in rows_sample for e in ids[r]))
+    w._experts = {(e, p): synth.expert_tensor(shape, e, p) for e in need for p in range(3)}
+    w.lazy = False
+    t0 = time.perf_counter()
+    moe_layer_from(w, x, rows=list(rows_sample))
+    dt = time.perf_counter() - t0
+    sub = step_bytes(shape, len(rows_sample), len(need))["layer"]
+    return dict(value=sub / dt / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{shape.name} step {step}, rows {list(rows_sample)} of {shape.rows} "
+                       f"({len(need)} experts + shared), float64 numpy oracle, {dt:.2f} s",
+                seconds=dt, us_per_step=dt * 1e6)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rows", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=8, help="device copies of the layer cycled by the steps")
+    ap.add_argument("--sweep-steps", type=int, default=100)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile", action="store_true", help="short run for rocprofv3: no sweep, no CPU leg")
+    ap.add_argument("--copy-calib", action="store_true", help="only run the plain copy kernel (PMC calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: there is no multi-GPU path in this library "
+              "(an expert-parallel split would give each GPU E/N experts and one all-reduce of the output)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_decode_gate_amd as moe
+    import synth
+    moe.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.copy_calib:
+        gbps, ms = copy_reference(1 << 30, reps=5)
+        log(f"[bench] copy 1 GiB: {ms:.3f} ms, {gbps:.0f} GB/s (read+write)")
+        return
+
+    if args.profile:
+        args.no_sweep, args.no_cpu = True, True
+
+    base_shape = synth.CONFIGS[WORKLOAD]
+    shape = base_shape.with_rows(args.rows) if args.rows != base_shape.rows else base_shape
+    cfg, layers = build_layers(base_shape, args.layers)
+    ws = torch.zeros(moe.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+
+    def inputs(rows):
+        return [torch.from_numpy(synth.activations(base_shape, s, rows=rows).view(np.int16)).cuda()
+                for s in range(N_INPUTS)]
+
+    xs = inputs(args.rows)
+    us = union_sizes(cfg, layers[0], xs, ws)
+    log(f"[bench] unions over {N_INPUTS} inputs: {us}")
+    res = timed_run(cfg, layers, xs, us, shape, args.rows, args.steps, args.warmup, ws)
+    log(f"[bench] rows={args.rows}: {res['us_per_step']:.1f} us/step, {res['gbps']:.0f} GB/s")
+
+    sweep = []
+    if not args.no_sweep:
+        for R in range(1, 9):
+            xr = inputs(R)
+            ur = union_sizes(cfg, layers[0], xr, ws)
+            r = timed_run(cfg, layers, xr, ur, base_shape.with_rows(R), R, args.sweep_steps, 10, ws,
+                          with_stage_events=False)
+            sweep.append(dict(rows=R, us_per_step=round(r["us_per_step"], 2), gbps=round(r["gbps"], 1),
+                              frac=round(r["gbps"] / HBM_PEAK_GBPS, 4), mean_union=r["mean_union"]))
+            log(f"[bench] sweep rows={R}: {r['us_per_step']:.1f} us/step {r['gbps']:.0f} GB/s U={r['mean_union']:.2f}")
+
+    copy_gbps, _ = copy_reference()
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(shape)
+        log(f"[bench] cpu oracle: {cpu['sample']}: {cpu['value']:.3f} GB/s")
+
+    dom = "gate_up_sweep"
+    st = res["stages"][dom]
+    line = {
+        "metric": METRIC,
+        "value": round(res["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["us_per_step"] / 1e3, 5),
+        "us_per_step": round(res["us_per_step"], 2),
+        "pct_peak": round(100 * res["gbps"] / HBM_PEAK_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: h=6144 E=256 top_k=8 I=Is=2048 rows={args.rows} "
+                               "sigmoid+bias rsf=2.5 NVFP4 experts, independent N(0,1) rows",
+                   "rows": args.rows, "layer_copies": args.layers, "inputs": N_INPUTS,
+                   "mean_union": res["mean_union"]},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(st["gbps"], 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(st["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_launch_us": round(st["avg_us"], 2), "bytes_per_launch": int(st["bytes_per_launch"])},
+        "stages_us": {k: round(v["avg_us"], 2) for k, v in res["stages"].items()},
+        "copy_gbps": round(copy_gbps, 1),
+        "sweep": sweep,
+        "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+/*
+ * moe.h -- C ABI of the routed mixture-of-experts layer for small-row decode
+ * and speculative-verify steps (rows = 1..8), built for AMD Instinct MI355X
+ * (gfx950) as libmoe.so.
+ *
+ * What is computed (sources are cited by page title and section):
+ *
+ *   "Function forward_moe" rustdoc, signature and summary: one routed MoE
+ *   site maps x[rows, h] to out[rows, h] given weights, a workspace and a
+ *   stream.  On one GPU ``out`` holds the full result (the page leaves a
+ *   partial sum only when experts or the shared expert are split over ranks).
+ *
+ *   metrale_model_layers/layers/moe/forward_token_major.rs,
+ *   MoeLayer::forward_token_major_decode: router GEMM over the rows; batched
+ *   top-k (softmax with norm_topk_prob, or sigmoid with a per-expert
+ *   correction bias, norm_topk_prob and routed_scaling_factor); expert
+ *   gate+up; silu(gate)*up and down; weighted sum plus the blend of the
+ *   shared expert gated by the input and shared_expert_gate.weight.  Experts
+ *   are untransposed NVFP4 matrices reached through device pointer tables of
+ *   packed codes, scales and scale2 values.
+ *
+ *   "Function forward_moe" rustdoc, "RETRACTED (2026-08-29)" and
+ *   "WIDENED (2026-08-31)" notes: the top_k*rows <= 64 selected ids are
+ *   deduplicated in one block by a pairwise scan (no sort), and each expert
+ *   of the union is swept once for all rows that chose it; rows <= 8.
+ *   SHARED-expert note: the shared expert runs once over all rows.
+ *
+ * Per row r:
+ *   L[r,e]   = sum_t x[r,t] * router_w[e,t]                     (fp32 result)
+ *   softmax: ids = top_k of L[r,:]; w = softmax weights of those ids,
+ *            renormalised over the k ids when norm_topk_prob.
+ *   sigmoid: s = sigmoid(L); ids = top_k of fp32(s + bias);
+ *            w = s[ids] (renormalised when norm_topk_prob) * routed_scaling_factor.
+ *   ids within a row are ordered by descending key, equal keys by lower id.
+ *   FFN_e(x) = W_down[e] @ (silu(W_gate[e] @ x) * (W_up[e] @ x))
+ *   out[r]   = bf16( sum_j w[r,j] * FFN_{ids[r,j]}(x_r)
+ *                    + sigmoid(x_r . shared_expert_gate) * FFN_shared(x_r) )
+ *
+ * NVFP4 matrix [n, k] ("untransposed": k contiguous):
+ *   packed  uint8 [n, k/2]   two E2M1 codes per byte, even column in the low nibble
+ *   scales  uint8 [n, k/16]  OCP E4M3FN scale for each 16 consecutive columns
+ *   scale2  fp32             per-tensor scale
+ *   W[i,t] = e2m1(code[i,t]) * e4m3(scales[i, t/16]) * scale2
+ * gate/up are [I, h], down is [h, I] (I = moe_inter or shared_inter).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are device pointers the caller allocates and owns.
+ *     The library keeps no pointer after a call returns and allocates no
+ *     device or host memory on any call.
+ *   - Calls validate on the host, enqueue kernels on ``stream`` (a
+ *     hipStream_t passed as void*, NULL = default stream) and return.  There
+ *     is no host synchronisation, no device-to-host copy and no host branch on
+ *     the routing, so every call can be captured into a HIP graph.  Results
+ *     are visible once the caller synchronises with the stream.
+ *   - Every argument error is reported before any HIP call.  No exception
+ *     crosses the ABI.  A non-OK status leaves a message for moe_last_error().
+ *   - One workspace serves one in-flight call.  Calls that share a workspace
+ *     must be ordered on one stream.
+ *   - Ids outside [0, num_experts) or repeated ids within a row, passed to
+ *     moe_union, are outside the contract (results are unspecified; the
+ *     kernels still read and write only in bounds of the documented buffers).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment, overlap or enum */
+  MOE_ERR_UNSUPPORTED = 2, /* a valid layer this library does not serve     */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes < moe_workspace_bytes(cfg)            */
+  MOE_ERR_DEVICE = 4       /* a HIP launch or runtime error                  */
+} moe_status;
+
+enum {
+  MOE_ROUTE_SOFTMAX = 0,      /* softmax top-k, optional renormalisation        */
+  MOE_ROUTE_SIGMOID_BIAS = 1, /* sigmoid + correction bias, routed_scaling_factor */
+  MOE_MAX_ROWS = 8,           /* rows per call ("WIDENED (2026-08-31)" note)     */
+  MOE_MAX_IDS = 64,           /* top_k * rows ("RETRACTED (2026-08-29)" note)    */
+  MOE_MAX_EXPERTS = 1024,     /* design cap on num_experts                       */
+  MOE_MAX_DIM = 8192,         /* cap on hidden, moe_inter and shared_inter       */
+  MOE_DIM_ALIGN = 32          /* hidden, moe_inter, shared_inter multiple of 32  */
+};
+
+/* Layer configuration (Glm5NextMlpConfig subset used by the routed path). */
+typedef struct moe_config {
+  int32_t hidden;               /* h                                            */
+  int32_t num_experts;          /* E, 1..MOE_MAX_EXPERTS                        */
+  int32_t top_k;                /* k, 1..E, and k * rows <= MOE_MAX_IDS         */
+  int32_t moe_inter;            /* I of a routed expert                          */
+  int32_t shared_inter;         /* Is of the shared expert                       */
+  int32_t route_kind;           /* MOE_ROUTE_SOFTMAX or MOE_ROUTE_SIGMOID_BIAS   */
+  int32_t norm_topk_prob;       /* 0 or 1                                        */
+  float routed_scaling_factor;  /* sigmoid routing only; softmax ignores it      */
+} moe_config;
+
+/* One NVFP4 matrix (layout above).  Both pointers 16-byte aligned. */
+typedef struct moe_nvfp4 {
+  const uint8_t* packed;
+  const uint8_t* scales;
+  float scale2;
+} moe_nvfp4;
+
+/* One projection of every routed expert, as device arrays indexed by expert
+ * id: packed[e] and scales[e] are device pointers (16-byte aligned) to
+ * expert e's matrix, scale2[e] its fp32 per-tensor scale.  The three arrays
+ * themselves live in device memory (forward_token_major.rs passes
+ * packed_ptrs, scale_ptrs and scale2_vals the same way). */
+typedef struct moe_expert_table {
+  const uint8_t* const* packed; /* device array [E] of device pointers */
+  const uint8_t* const* scales; /* device array [E] of device pointers */
+  const float* scale2;          /* device array [E]                    */
+} moe_expert_table;
+
+typedef struct moe_weights {
+  const float* router_w;           /* [E, h] fp32, row-major                    */
+  const float* correction_bias;    /* [E] fp32 for SIGMOID_BIAS, NULL otherwise  */
+  moe_expert_table gate;           /* [I, h] per expert                          */
+  moe_expert_table up;             /* [I, h] per expert                          */
+  moe_expert_table down;           /* [h, I] per expert                          */
+  moe_nvfp4 shared_gate;           /* [Is, h]                                    */
+  moe_nvfp4 shared_up;             /* [Is, h]                                    */
+  moe_nvfp4 shared_down;           /* [h, Is]                                    */
+  const float* shared_expert_gate; /* [h] fp32: gate = sigmoid(x . this)        */
+} moe_weights;
+
+/* Byte offsets of the intermediates moe_forward leaves in the workspace.
+ * The layout depends on the config only (sized for MOE_MAX_ROWS rows).
+ * Offsets are multiples of 256. */
+typedef struct moe_ws_layout {
+  size_t partials;      /* double [nkc][MOE_MAX_ROWS][E+1] router K-chunk partial dots */
+  size_t logits;        /* float  [MOE_MAX_ROWS][E]   router logits (row stride E)    */
+  size_t gamma;         /* float  [MOE_MAX_ROWS]      sigmoid(x_r . shared gate)      */
+  size_t topk_ids;      /* int32  [MOE_MAX_ROWS][k]   (row stride k)                  */
+  size_t topk_w;        /* float  [MOE_MAX_ROWS][k]                                   */
+  size_t union_ids;     /* int32  [MOE_MAX_IDS]       first-occurrence order          */
+  size_t union_count;   /* int32  [1]                 U                               */
+  size_t slot_to_union; /* int32  [MOE_MAX_IDS]       slot t = r*k + j -> union index */
+  size_t row_mask;      /* uint32 [MOE_MAX_IDS]       bit r: row r chose union expert */
+  size_t slot_info;     /* internal per-union-slot weight pointers                    */
+  size_t act;           /* bf16   [MOE_MAX_IDS+1][MOE_MAX_ROWS][Imax] silu(g)*u,
+                           slot MOE_MAX_IDS = shared expert, Imax = max(I, Is)       */
+  size_t y;             /* float  [MOE_MAX_IDS+1][MOE_MAX_ROWS][h] expert outputs     */
+  size_t total;         /* bytes needed                                               */
+} moe_ws_layout;
+
+/* Workspace bytes for ``cfg`` (any rows up to MOE_MAX_ROWS); 0 if cfg is invalid. */
+size_t moe_workspace_bytes(const moe_config* cfg);
+
+/* Fill ``out`` with the workspace layout of ``cfg``. */
+moe_status moe_workspace_layout(const moe_config* cfg, moe_ws_layout* out);
+
+/* Router and top-k routing (forward_token_major.rs: router GEMM, then
+ * moe_topk_sigmoid_batched or moe_topk_softmax_batched; forward_ep.rs: the
+ * one-row GEMV and moe_topk_softmax).
+ *   x_bf16    [rows, h] bf16 bits, 16-byte aligned
+ *   topk_ids  [rows, k] int32 out, ordered by descending key, ties by lower id
+ *   topk_w    [rows, k] fp32 out
+ * Also leaves partials, logits and gamma in the workspace. */
+moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                     int32_t rows, int32_t* topk_ids, float* topk_w,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Union of the experts selected by ``rows`` rows ("Function forward_moe"
+ * rustdoc, "RETRACTED (2026-08-29)" note: one block, pairwise scan, no sort).
+ *   topk_ids       [rows, top_k] int32 in, each row's ids distinct, in [0, num_experts)
+ *   union_ids      [MOE_MAX_IDS] out, first occurrence in row-major slot order
+ *   union_count    [1] out, U
+ *   slot_to_union  [rows*top_k] out, union position of slot t = r*top_k + j
+ *   row_mask       [MOE_MAX_IDS] out, bit r set when row r chose union expert u;
+ *                  may be NULL
+ * Entries of union_ids and row_mask at positions >= U are left untouched. */
+moe_status moe_union(const int32_t* topk_ids, int32_t rows, int32_t top_k, int32_t num_experts,
+                     int32_t* union_ids, int32_t* union_count, int32_t* slot_to_union,
+                     uint32_t* row_mask, void* stream);
+
+/* The whole layer: x[rows, h] bf16 -> out[rows, h] bf16 (overwritten, not
+ * accumulated).  x and out 16-byte aligned and not overlapping.  Leaves every
+ * intermediate of moe_ws_layout in the workspace.  Each row's output depends
+ * on that row's input alone: a call with R rows writes, for every row, the
+ * same bytes as a one-row call with that row. */
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                       uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward that also records ``stage_events[i]`` (a hipEvent_t, may be
+ * NULL) on ``stream`` before stage i, and ``stage_events[moe_num_stages()]``
+ * after the last stage: per-stage timing without changing the work.
+ * ``stage_events`` itself may be NULL (then identical to moe_forward). */
+moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                             uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes,
+                             void* stream, void* const* stage_events);
+
+/* Number of kernel stages moe_forward enqueues, and the name of stage i
+ * (NULL when out of range). */
+int32_t moe_num_stages(void);
+const char* moe_stage_name(int32_t i);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,353 @@
+// C ABI of libmoe: argument validation, workspace layout and stage launches.
+//
+// Every refusal happens here, before any HIP call, and leaves a message for
+// moe_last_error() -- the C form of the refusals the pages make with a message
+// (forward_token_major.rs and forward_ep.rs refuse a router whose width differs
+// from num_experts; forward_token_major.rs routes layers without a shared
+// expert or with other formats to another path).
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+const char* const kStageNames[] = {"router_gemv", "topk_union", "gate_up_sweep", "down_sweep", "blend"};
+constexpr int kNumStages = 5;
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->hidden < MOE_DIM_ALIGN || c->hidden > MOE_MAX_DIM || c->hidden % MOE_DIM_ALIGN)
+    return fail(MOE_ERR_INVALID_ARG, "hidden=%d must be a multiple of %d in [%d, %d]", c->hidden, MOE_DIM_ALIGN,
+                MOE_DIM_ALIGN, MOE_MAX_DIM);
+  if (c->moe_inter < MOE_DIM_ALIGN || c->moe_inter > MOE_MAX_DIM || c->moe_inter % MOE_DIM_ALIGN)
+    return fail(MOE_ERR_INVALID_ARG, "moe_inter=%d must be a multiple of %d in [%d, %d]", c->moe_inter,
+                MOE_DIM_ALIGN, MOE_DIM_ALIGN, MOE_MAX_DIM);
+  if (c->shared_inter < MOE_DIM_ALIGN || c->shared_inter > MOE_MAX_DIM || c->shared_inter % MOE_DIM_ALIGN)
+    return fail(MOE_ERR_INVALID_ARG, "shared_inter=%d must be a multiple of %d in [%d, %d]", c->shared_inter,
+                MOE_DIM_ALIGN, MOE_DIM_ALIGN, MOE_MAX_DIM);
+  if (c->num_experts < 1 || c->num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts=%d outside [1, %d]", c->num_experts, MOE_MAX_EXPERTS);
+  if (c->top_k < 1 || c->top_k > c->num_experts || c->top_k > MOE_MAX_IDS)
+    return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside [1, min(num_experts=%d, %d)]", c->top_k, c->num_experts,
+                MOE_MAX_IDS);
+  if (c->route_kind != MOE_ROUTE_SOFTMAX && c->route_kind != MOE_ROUTE_SIGMOID_BIAS)
+    return fail(MOE_ERR_INVALID_ARG, "unknown route_kind %d", c->route_kind);
+  if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1)
+    return fail(MOE_ERR_INVALID_ARG, "norm_topk_prob=%d must be 0 or 1", c->norm_topk_prob);
+  const float rsf = c->routed_scaling_factor;
+  if (!(rsf == rsf) || rsf > 3.0e38f || rsf < -3.0e38f)
+    return fail(MOE_ERR_INVALID_ARG, "routed_scaling_factor is not finite");
+  return MOE_OK;
+}
+
+moe_status check_rows(const moe_config* c, int32_t rows) {
+  if (rows < 1 || rows > MOE_MAX_ROWS)
+    return fail(MOE_ERR_INVALID_ARG, "rows=%d outside [1, %d]", rows, MOE_MAX_ROWS);
+  if (c->top_k * rows > MOE_MAX_IDS)
+    return fail(MOE_ERR_INVALID_ARG, "top_k*rows=%d exceeds the %d ids one block deduplicates", c->top_k * rows,
+                MOE_MAX_IDS);
+  return MOE_OK;
+}
+
+moe_status check_nvfp4(const moe_nvfp4& t, const char* name) {
+  if (!t.packed || !t.scales) return fail(MOE_ERR_UNSUPPORTED, "%s: the layer has no shared expert", name);
+  if (!aligned(t.packed, 16) || !aligned(t.scales, 16))
+    return fail(MOE_ERR_INVALID_ARG, "%s: packed and scales must be 16-byte aligned", name);
+  if (!(t.scale2 == t.scale2)) return fail(MOE_ERR_INVALID_ARG, "%s: scale2 is NaN", name);
+  return MOE_OK;
+}
+
+moe_status check_table(const moe_expert_table& t, const char* name) {
+  if (!t.packed || !t.scales || !t.scale2) return fail(MOE_ERR_INVALID_ARG, "%s table has a NULL array", name);
+  if (!aligned(t.packed, 8) || !aligned(t.scales, 8) || !aligned(t.scale2, 4))
+    return fail(MOE_ERR_INVALID_ARG, "%s table arrays are misaligned", name);
+  return MOE_OK;
+}
+
+moe_status check_route_weights(const moe_config* c, const moe_weights* w) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->router_w || !aligned(w->router_w, 16))
+    return fail(MOE_ERR_INVALID_ARG, "router_w must be a 16-byte aligned device pointer");
+  if (c->route_kind == MOE_ROUTE_SIGMOID_BIAS) {
+    if (!w->correction_bias || !aligned(w->correction_bias, 4))
+      return fail(MOE_ERR_INVALID_ARG, "sigmoid routing needs an aligned correction_bias");
+  } else if (w->correction_bias) {
+    return fail(MOE_ERR_INVALID_ARG, "softmax routing takes no correction_bias");
+  }
+  if (!w->shared_expert_gate)
+    return fail(MOE_ERR_UNSUPPORTED, "shared_expert_gate is NULL (ungated shared expert not served)");
+  if (!aligned(w->shared_expert_gate, 16))
+    return fail(MOE_ERR_INVALID_ARG, "shared_expert_gate must be 16-byte aligned");
+  return MOE_OK;
+}
+
+moe_status check_all_weights(const moe_config* c, const moe_weights* w) {
+  moe_status st = check_route_weights(c, w);
+  if (st) return st;
+  if ((st = check_nvfp4(w->shared_gate, "shared_gate"))) return st;
+  if ((st = check_nvfp4(w->shared_up, "shared_up"))) return st;
+  if ((st = check_nvfp4(w->shared_down, "shared_down"))) return st;
+  if ((st = check_table(w->gate, "gate"))) return st;
+  if ((st = check_table(w->up, "up"))) return st;
+  if ((st = check_table(w->down, "down"))) return st;
+  return MOE_OK;
+}
+
+void compute_layout(const moe_config* c, moe_ws_layout* L) {
+  const size_t R = MOE_MAX_ROWS, E = (size_t)c->num_experts, k = (size_t)c->top_k, h = (size_t)c->hidden;
+  const size_t nkc = (h + 2047) / 2048;
+  const size_t imax = (size_t)(c->moe_inter > c->shared_inter ? c->moe_inter : c->shared_inter);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  L->partials = take(nkc * R * (E + 1) * sizeof(double));
+  L->logits = take(R * E * sizeof(float));
+  L->gamma = take(R * sizeof(float));
+  L->topk_ids = take(R * k * sizeof(int32_t));
+  L->topk_w = take(R * k * sizeof(float));
+  L->union_ids = take(MOE_MAX_IDS * sizeof(int32_t));
+  L->union_count = take(sizeof(int32_t));
+  L->slot_to_union = take(MOE_MAX_IDS * sizeof(int32_t));
+  L->row_mask = take(MOE_MAX_IDS * sizeof(uint32_t));
+  L->slot_info = take((MOE_MAX_IDS + 1) * moe::kSlotInfoBytes);
+  L->act = take((MOE_MAX_IDS + 1) * R * imax * sizeof(uint16_t));
+  L->y = take((MOE_MAX_IDS + 1) * R * h * sizeof(float));
+  L->total = off;
+}
+
+moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes, moe_ws_layout* L) {
+  compute_layout(c, L);
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "ws is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  if (ws_bytes < L->total)
+    return fail(MOE_ERR_WORKSPACE, "ws_bytes=%zu < %zu required", ws_bytes, L->total);
+  return MOE_OK;
+}
+
+moe_status check_xy(const moe_config* c, const uint16_t* x, const uint16_t* out, int32_t rows, void* ws,
+                    const moe_ws_layout& L) {
+  const size_t xb = (size_t)rows * c->hidden * sizeof(uint16_t);
+  if (!x || !aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x must be a 16-byte aligned device pointer");
+  if (overlaps(x, xb, ws, L.total)) return fail(MOE_ERR_INVALID_ARG, "x overlaps the workspace");
+  if (out) {
+    if (!aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    if (overlaps(x, xb, out, xb)) return fail(MOE_ERR_INVALID_ARG, "x and out overlap");
+    if (overlaps(out, xb, ws, L.total)) return fail(MOE_ERR_INVALID_ARG, "out overlaps the workspace");
+  }
+  return MOE_OK;
+}
+
+moe_status device_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+void fill_topk(moe::TopkParams& p, const moe_config* c, const moe_weights* w, int32_t rows, char* ws,
+               const moe_ws_layout& L, int32_t* ids_out, float* w_out) {
+  memset(&p, 0, sizeof p);
+  p.partials = reinterpret_cast<const double*>(ws + L.partials);
+  p.nkc = (c->hidden + 2047) / 2048;
+  p.bias = w->correction_bias;
+  p.E = c->num_experts;
+  p.k = c->top_k;
+  p.rows = rows;
+  p.route_kind = c->route_kind;
+  p.norm = c->norm_topk_prob;
+  p.rsf = c->routed_scaling_factor;
+  p.logits = reinterpret_cast<float*>(ws + L.logits);
+  p.gamma = reinterpret_cast<float*>(ws + L.gamma);
+  p.ids_out = ids_out;
+  p.w_out = w_out;
+  p.union_ids = reinterpret_cast<int32_t*>(ws + L.union_ids);
+  p.union_count = reinterpret_cast<int32_t*>(ws + L.union_count);
+  p.slot_to_union = reinterpret_cast<int32_t*>(ws + L.slot_to_union);
+  p.row_mask = reinterpret_cast<uint32_t*>(ws + L.row_mask);
+  p.slots = reinterpret_cast<moe::SlotInfo*>(ws + L.slot_info);
+  p.gate = w->gate;
+  p.up = w->up;
+  p.down = w->down;
+  p.shared_gate = w->shared_gate;
+  p.shared_up = w->shared_up;
+  p.shared_down = w->shared_down;
+  p.inter = c->moe_inter;
+  p.shared_inter = c->shared_inter;
+}
+
+moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint16_t* x, uint16_t* out,
+                        int32_t rows, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  moe_status st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_rows(cfg, rows))) return st;
+  if ((st = check_all_weights(cfg, w))) return st;
+  moe_ws_layout L;
+  if ((st = check_ws(cfg, ws, ws_bytes, &L))) return st;
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  if ((st = check_xy(cfg, x, out, rows, ws, L))) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  auto mark = [&](int i) -> hipError_t {
+    if (events && events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s);
+    return hipSuccess;
+  };
+  const int max_union = cfg->top_k * rows < cfg->num_experts ? cfg->top_k * rows : cfg->num_experts;
+
+  moe::TopkParams tp;
+  int32_t* ids = reinterpret_cast<int32_t*>(wsb + L.topk_ids);
+  float* wts = reinterpret_cast<float*>(wsb + L.topk_w);
+  fill_topk(tp, cfg, w, rows, wsb, L, ids, wts);
+
+  moe::SweepParams sp;
+  sp.x = x;
+  sp.slots = reinterpret_cast<const moe::SlotInfo*>(wsb + L.slot_info);
+  sp.union_count = reinterpret_cast<const int32_t*>(wsb + L.union_count);
+  sp.act = reinterpret_cast<uint16_t*>(wsb + L.act);
+  sp.y = reinterpret_cast<float*>(wsb + L.y);
+  sp.h = cfg->hidden;
+  sp.act_stride = cfg->moe_inter > cfg->shared_inter ? cfg->moe_inter : cfg->shared_inter;
+  sp.inter = cfg->moe_inter;
+  sp.shared_inter = cfg->shared_inter;
+
+  hipError_t e;
+  if ((e = mark(0)) != hipSuccess) return device_status(e, "event record");
+  e = moe::launch_router(x, w->router_w, w->shared_expert_gate, reinterpret_cast<double*>(wsb + L.partials),
+                         rows, cfg->hidden, cfg->num_experts, s);
+  if (e != hipSuccess) return device_status(e, "router launch");
+  if ((e = mark(1)) != hipSuccess) return device_status(e, "event record");
+  if ((e = moe::launch_topk(tp, true, s)) != hipSuccess) return device_status(e, "top-k launch");
+  if ((e = mark(2)) != hipSuccess) return device_status(e, "event record");
+  if ((e = moe::launch_gateup(sp, rows, max_union, s)) != hipSuccess) return device_status(e, "gate/up launch");
+  if ((e = mark(3)) != hipSuccess) return device_status(e, "event record");
+  if ((e = moe::launch_down(sp, rows, max_union, s)) != hipSuccess) return device_status(e, "down launch");
+  if ((e = mark(4)) != hipSuccess) return device_status(e, "event record");
+  e = moe::launch_blend(sp.y, wts, tp.slot_to_union, tp.gamma, out, rows, cfg->hidden, cfg->top_k, s);
+  if (e != hipSuccess) return device_status(e, "blend launch");
+  if ((e = mark(5)) != hipSuccess) return device_status(e, "event record");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config* cfg) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  moe_ws_layout L;
+  compute_layout(cfg, &L);
+  return L.total;
+}
+
+moe_status moe_workspace_layout(const moe_config* cfg, moe_ws_layout* out) {
+  moe_status st = check_config(cfg);
+  if (st) return st;
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  compute_layout(cfg, out);
+  return ok();
+}
+
+moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16, int32_t rows,
+                     int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_rows(cfg, rows))) return st;
+  if ((st = check_route_weights(cfg, w))) return st;
+  moe_ws_layout L;
+  if ((st = check_ws(cfg, ws, ws_bytes, &L))) return st;
+  if ((st = check_xy(cfg, x_bf16, nullptr, rows, ws, L))) return st;
+  if (!topk_ids || !aligned(topk_ids, 4) || !topk_w || !aligned(topk_w, 4))
+    return fail(MOE_ERR_INVALID_ARG, "topk_ids and topk_w must be aligned device pointers");
+  const size_t nb = (size_t)rows * cfg->top_k * 4;
+  if (overlaps(topk_ids, nb, topk_w, nb)) return fail(MOE_ERR_INVALID_ARG, "topk_ids and topk_w overlap");
+  char* wsb = static_cast<char*>(ws);
+  if (overlaps(topk_ids, nb, wsb, L.topk_ids) || overlaps(topk_w, nb, wsb, L.topk_ids))
+    return fail(MOE_ERR_INVALID_ARG, "topk outputs overlap the router intermediates of the workspace");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  moe::TopkParams tp;
+  fill_topk(tp, cfg, w, rows, wsb, L, topk_ids, topk_w);
+  hipError_t e = moe::launch_router(x_bf16, w->router_w, w->shared_expert_gate,
+                                    reinterpret_cast<double*>(wsb + L.partials), rows, cfg->hidden,
+                                    cfg->num_experts, s);
+  if (e != hipSuccess) return device_status(e, "router launch");
+  if ((e = moe::launch_topk(tp, false, s)) != hipSuccess) return device_status(e, "top-k launch");
+  return ok();
+}
+
+moe_status moe_union(const int32_t* topk_ids, int32_t rows, int32_t top_k, int32_t num_experts,
+                     int32_t* union_ids, int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask,
+                     void* stream) {
+  if (rows < 1 || rows > MOE_MAX_ROWS) return fail(MOE_ERR_INVALID_ARG, "rows=%d outside [1, %d]", rows, MOE_MAX_ROWS);
+  if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts=%d outside [1, %d]", num_experts, MOE_MAX_EXPERTS);
+  if (top_k < 1 || top_k > num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside [1, num_experts=%d]", top_k, num_experts);
+  if (top_k * rows > MOE_MAX_IDS)
+    return fail(MOE_ERR_INVALID_ARG, "top_k*rows=%d exceeds %d", top_k * rows, MOE_MAX_IDS);
+  if (!topk_ids || !union_ids || !union_count || !slot_to_union)
+    return fail(MOE_ERR_INVALID_ARG, "NULL id buffer");
+  if (!aligned(topk_ids, 4) || !aligned(union_ids, 4) || !aligned(union_count, 4) || !aligned(slot_to_union, 4) ||
+      (row_mask && !aligned(row_mask, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "id buffers must be 4-byte aligned");
+  const size_t n = (size_t)rows * top_k * 4;
+  if (overlaps(union_ids, MOE_MAX_IDS * 4, slot_to_union, n) || overlaps(union_count, 4, union_ids, MOE_MAX_IDS * 4) ||
+      overlaps(union_count, 4, slot_to_union, n) ||
+      (row_mask && (overlaps(row_mask, MOE_MAX_IDS * 4, union_ids, MOE_MAX_IDS * 4) ||
+                    overlaps(row_mask, MOE_MAX_IDS * 4, slot_to_union, n) || overlaps(row_mask, MOE_MAX_IDS * 4, union_count, 4))))
+    return fail(MOE_ERR_INVALID_ARG, "union output buffers overlap");
+  hipError_t e = moe::launch_union(topk_ids, rows, top_k, union_ids, union_count, slot_to_union, row_mask,
+                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_status(e, "union launch");
+  return ok();
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16, uint16_t* out_bf16,
+                       int32_t rows, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                             uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream,
+                             void* const* stage_events) {
+  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, stage_events);
+}
+
+int32_t moe_num_stages(void) { return kNumStages; }
+
+const char* moe_stage_name(int32_t i) { return (i >= 0 && i < kNumStages) ? kStageNames[i] : nullptr; }
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

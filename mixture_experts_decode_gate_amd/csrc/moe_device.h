@@ -1,0 +1,114 @@
+// Device-side helpers shared by the routed-MoE kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kChunk = 2048;        // K columns one wave covers per pass: 64 lanes x 32 columns
+constexpr int kChunkUnits = 256;    // 16-byte bf16 units per chunk (2048 * 2 B / 16 B)
+constexpr int kMaxRows = 8;
+constexpr int kMaxIds = 64;
+constexpr int kSharedSlot = 64;     // act / y / slot_info index of the shared expert
+constexpr int kNumSlots = 65;
+
+// Weight pointers of one union slot (a routed expert, or the shared expert at
+// kSharedSlot), resolved once per call so the sweeps need a single load.
+struct SlotInfo {
+  const uint8_t* gate_packed;
+  const uint8_t* gate_scales;
+  const uint8_t* up_packed;
+  const uint8_t* up_scales;
+  const uint8_t* down_packed;
+  const uint8_t* down_scales;
+  float gate_scale2;
+  float up_scale2;
+  float down_scale2;
+  int32_t inter;      // rows of gate/up, columns of down
+  uint32_t row_mask;  // bit r: row r uses this slot
+  int32_t expert;     // expert id, -1 for the shared expert
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round to nearest even; inputs are finite.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+// Two E2M1 codes (byte SEL of w, low nibble first) -> two bf16 values.  The
+// hardware conversion is exact: every E2M1 value is a bf16 value.
+template <int SEL>
+__device__ __forceinline__ bf16x2 e2m1x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL);
+}
+
+// OCP E4M3FN byte SEL of w -> fp32 (exact).
+template <int SEL>
+__device__ __forceinline__ float e4m3(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
+__device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// Butterfly sum over the 64 lanes.  Lanes may differ in the last bit; callers
+// take lane 0's value so the result is deterministic.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Decode 32 E2M1 codes (one 16-byte load) into 16 bf16 pairs, column order.
+__device__ __forceinline__ void decode32(const u32x4& q, bf16x2 (&w)[16]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    w[d * 4 + 0] = e2m1x2<0>(q[d]);
+    w[d * 4 + 1] = e2m1x2<1>(q[d]);
+    w[d * 4 + 2] = e2m1x2<2>(q[d]);
+    w[d * 4 + 3] = e2m1x2<3>(q[d]);
+  }
+}
+
+// Dot of 32 decoded weights with 32 bf16 activations (4 units of 8), applying
+// each 16-column block scale once: s0 * (cols 0..15) + s1 * (cols 16..31),
+// accumulated into acc in that order.
+__device__ __forceinline__ float dot32(const bf16x2 (&w)[16], const u32x4& x0, const u32x4& x1,
+                                       const u32x4& x2, const u32x4& x3, float s0, float s1, float acc) {
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) p0 = dot2(w[b], as_bf16x2(x0[b]), p0);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) p0 = dot2(w[4 + b], as_bf16x2(x1[b]), p0);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) p1 = dot2(w[8 + b], as_bf16x2(x2[b]), p1);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) p1 = dot2(w[12 + b], as_bf16x2(x3[b]), p1);
+  acc = __builtin_fmaf(s0, p0, acc);
+  acc = __builtin_fmaf(s1, p1, acc);
+  return acc;
+}
+
+// LDS position of natural 16-byte unit `u` (0..255) of a 2048-column chunk.
+// Lane l reads units 4l..4l+3; storing unit u at (u & 3) * 64 + (u >> 2) makes
+// each of the four reads cover 64 consecutive units (no bank conflicts).
+__device__ __forceinline__ int swz_unit(int u) { return (u & 3) * 64 + (u >> 2); }
+
+}  // namespace moe

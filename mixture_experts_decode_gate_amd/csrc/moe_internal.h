@@ -1,0 +1,58 @@
+// Host <-> kernel interface of libmoe (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+struct SlotInfo;
+
+struct TopkParams {
+  const double* partials;  // [nkc][8][E+1]
+  int nkc;
+  const float* bias;       // [E] or null (softmax)
+  int E, k, rows, route_kind, norm;
+  float rsf;
+  float* logits;           // [8][E]
+  float* gamma;            // [8]
+  int32_t* ids_out;        // [rows][k]
+  float* w_out;            // [rows][k]
+  // union outputs (moe_forward only)
+  int32_t* union_ids;
+  int32_t* union_count;
+  int32_t* slot_to_union;
+  uint32_t* row_mask;
+  SlotInfo* slots;         // [65]
+  moe_expert_table gate, up, down;
+  moe_nvfp4 shared_gate, shared_up, shared_down;
+  int inter, shared_inter;
+};
+
+struct SweepParams {
+  const uint16_t* x;          // [rows][h] bf16
+  const SlotInfo* slots;      // [65]
+  const int32_t* union_count; // device U
+  uint16_t* act;              // [65][8][act_stride] bf16
+  float* y;                   // [65][8][h] fp32
+  int h;
+  int act_stride;             // max(inter, shared_inter)
+  int inter;                  // routed expert intermediate size
+  int shared_inter;
+};
+
+constexpr size_t kSlotInfoBytes = 72;  // sizeof(SlotInfo), checked in the kernels file
+
+hipError_t launch_router(const uint16_t* x, const float* router_w, const float* gate_vec, double* partials,
+                         int rows, int h, int E, hipStream_t s);
+hipError_t launch_topk(const TopkParams& p, bool with_union, hipStream_t s);
+hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids, int32_t* union_count,
+                        int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);
+hipError_t launch_gateup(const SweepParams& p, int rows, int max_union, hipStream_t s);
+hipError_t launch_down(const SweepParams& p, int rows, int max_union, hipStream_t s);
+hipError_t launch_blend(const float* y, const float* w, const int32_t* slot_to_union, const float* gamma,
+                        uint16_t* out, int rows, int h, int k, hipStream_t s);
+
+}  // namespace moe

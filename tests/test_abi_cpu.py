@@ -1,0 +1,169 @@
+"""C ABI of libmoe.so on the CPU: exports and argument refusals (no GPU calls).
+
+Every refusal below happens before any HIP call, so these tests run in a
+container without a GPU.  Device pointers are fake, aligned addresses that
+the library never dereferences on these paths.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("mixture_experts_decode_gate_amd")
+if not os.path.exists(moe.LIB_PATH):
+    pytest.skip("libmoe.so not built", allow_module_level=True)
+
+lib = moe.load()
+
+BASE = 0x7F0000000000  # fake device addresses, 256-byte aligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert {"moe_route", "moe_union", "moe_forward", "moe_workspace_bytes", "moe_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def cfg_c4(**kw):
+    c = moe.MoeConfig(6144, 256, 8, 2048, 2048, moe.MOE_ROUTE_SIGMOID_BIAS, 1, 2.5)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def fake_weights(sigmoid=True):
+    w = moe.MoeWeights()
+    w.router_w = BASE + 0x1000
+    w.correction_bias = (BASE + 0x2000) if sigmoid else 0
+    for i, name in enumerate(("gate", "up", "down")):
+        setattr(w, name, moe.MoeExpertTable(BASE + 0x10000 * (i + 1), BASE + 0x10000 * (i + 1) + 0x4000,
+                                            BASE + 0x10000 * (i + 1) + 0x8000))
+    for i, name in enumerate(("shared_gate", "shared_up", "shared_down")):
+        setattr(w, name, moe.MoeNvfp4(BASE + 0x100000 * (i + 1), BASE + 0x100000 * (i + 1) + 0x40000, 1.0))
+    w.shared_expert_gate = BASE + 0x3000
+    return w
+
+
+WS = BASE + 0x10000000
+X = BASE + 0x20000000
+OUT = BASE + 0x30000000
+
+
+def forward(cfg, w, x=X, out=OUT, rows=4, ws=WS, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.moe_workspace_bytes(ctypes.byref(cfg)) or 1
+    return lib.moe_forward(ctypes.byref(cfg), ctypes.byref(w) if w is not None else None, x, out, rows, ws,
+                           ws_bytes, None)
+
+
+def test_workspace_layout_is_ordered_and_aligned():
+    cfg = cfg_c4()
+    L = moe.moe_workspace_layout(cfg)
+    names = [f[0] for f in moe.MoeWsLayout._fields_]
+    offs = [getattr(L, n) for n in names]
+    assert offs == sorted(offs) and len(set(offs)) == len(offs)
+    assert all(o % 256 == 0 for o in offs)
+    assert L.total == moe.moe_workspace_bytes(cfg)
+    # act holds 65 slots x 8 rows x max(I, Is) bf16; y 65 x 8 x h fp32
+    assert L.y - L.act >= 65 * 8 * 2048 * 2
+    assert L.total - L.y >= 65 * 8 * 6144 * 4
+    assert lib.moe_workspace_bytes(ctypes.byref(cfg_c4(hidden=100))) == 0
+
+
+@pytest.mark.parametrize("field,value", [
+    ("hidden", 0), ("hidden", 100), ("hidden", 16384), ("moe_inter", 48), ("shared_inter", 0),
+    ("num_experts", 0), ("num_experts", 2048), ("top_k", 0), ("top_k", 257), ("route_kind", 7),
+    ("norm_topk_prob", 2), ("routed_scaling_factor", float("nan")),
+])
+def test_bad_config_refused(field, value):
+    cfg = cfg_c4(**{field: value})
+    assert forward(cfg, fake_weights(), ws_bytes=1 << 30) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_last_error().decode()
+
+
+@pytest.mark.parametrize("rows", [0, 9, -1])
+def test_bad_rows_refused(rows):
+    assert forward(cfg_c4(), fake_weights(), rows=rows) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_too_many_ids_refused():
+    # top_k * rows > 64: more ids than one block deduplicates
+    assert forward(cfg_c4(top_k=16), fake_weights(), rows=5) == moe.MOE_ERR_INVALID_ARG
+    assert "64" in lib.moe_last_error().decode()
+
+
+def test_pointer_refusals():
+    cfg = cfg_c4()
+    assert forward(cfg, None) == moe.MOE_ERR_INVALID_ARG
+    assert forward(cfg, fake_weights(), x=0) == moe.MOE_ERR_INVALID_ARG
+    assert forward(cfg, fake_weights(), out=0) == moe.MOE_ERR_INVALID_ARG
+    assert forward(cfg, fake_weights(), x=X + 8) == moe.MOE_ERR_INVALID_ARG        # misaligned
+    assert forward(cfg, fake_weights(), out=X + 64) == moe.MOE_ERR_INVALID_ARG     # overlaps x
+    assert forward(cfg, fake_weights(), ws=WS + 16) == moe.MOE_ERR_INVALID_ARG     # ws alignment
+    assert forward(cfg, fake_weights(), x=WS + 1024) == moe.MOE_ERR_INVALID_ARG    # x inside ws
+    w = fake_weights()
+    w.router_w = BASE + 0x1004
+    assert forward(cfg, w) == moe.MOE_ERR_INVALID_ARG
+    w = fake_weights()
+    w.up = moe.MoeExpertTable(0, 0, 0)
+    assert forward(cfg, w) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_bias_must_match_route_kind():
+    assert forward(cfg_c4(), fake_weights(sigmoid=False)) == moe.MOE_ERR_INVALID_ARG
+    assert forward(cfg_c4(route_kind=moe.MOE_ROUTE_SOFTMAX), fake_weights(sigmoid=True)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_unsupported_layers():
+    w = fake_weights()
+    w.shared_up = moe.MoeNvfp4(0, 0, 1.0)          # no shared expert
+    assert forward(cfg_c4(), w) == moe.MOE_ERR_UNSUPPORTED
+    w = fake_weights()
+    w.shared_expert_gate = 0                       # ungated shared expert
+    assert forward(cfg_c4(), w) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_small_workspace_refused():
+    cfg = cfg_c4()
+    need = lib.moe_workspace_bytes(ctypes.byref(cfg))
+    assert forward(cfg, fake_weights(), ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+
+
+def test_union_refusals():
+    u = lambda rows, k, E, ids=X, uid=OUT, cnt=OUT + 512, s2u=OUT + 1024, rm=OUT + 2048: lib.moe_union(
+        ids, rows, k, E, uid, cnt, s2u, rm, None)
+    assert u(0, 8, 256) == moe.MOE_ERR_INVALID_ARG
+    assert u(9, 1, 256) == moe.MOE_ERR_INVALID_ARG
+    assert u(8, 9, 256) == moe.MOE_ERR_INVALID_ARG      # 72 ids
+    assert u(2, 8, 4) == moe.MOE_ERR_INVALID_ARG        # top_k > num_experts
+    assert u(1, 8, 256, ids=0) == moe.MOE_ERR_INVALID_ARG
+    assert u(1, 8, 256, s2u=OUT + 64) == moe.MOE_ERR_INVALID_ARG  # overlaps union_ids
+
+
+def test_route_refusals():
+    cfg = cfg_c4()
+    need = lib.moe_workspace_bytes(ctypes.byref(cfg))
+    r = lambda ids, wts, rows=2: lib.moe_route(ctypes.byref(cfg), ctypes.byref(fake_weights()), X, rows, ids,
+                                               wts, WS, need, None)
+    assert r(0, OUT) == moe.MOE_ERR_INVALID_ARG
+    assert r(OUT, OUT + 16) == moe.MOE_ERR_INVALID_ARG   # ids and weights overlap
+    assert r(OUT, OUT + 4096, rows=9) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_stage_names():
+    n = lib.moe_num_stages()
+    assert n >= 1
+    assert [lib.moe_stage_name(i) is not None for i in range(n)] == [True] * n
+    assert lib.moe_stage_name(n) is None and lib.moe_stage_name(-1) is None

@@ -1,0 +1,238 @@
+"""GPU parity of the whole layer (moe_forward) against the oracle.
+
+* small configurations: every row, every intermediate;
+* the 256-expert configurations at full size: routing and the union for all
+  rows, expert outputs on sampled rows the oracle evaluates one by one;
+* stage checks with block scales over every finite E4M3FN byte: the gate/up
+  activations against a float64 recomputation from the same x, the down
+  outputs against a float64 recomputation from the kernel's own activations;
+* ragged shapes (partial 2048-column chunks), top_k = E, 64 ids;
+* a call with R rows equals R one-row calls byte for byte ("Function
+  forward_moe" rustdoc, "RETRACTED (2026-08-29)" note: byte-identical either
+  way); two runs are identical; a captured HIP graph replays identically.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from oracle.formats import E4M3FN_TABLE, dequant_nvfp4, f32_to_bf16_bits
+from oracle.layer import moe_layer_from
+from oracle.ffn import silu
+
+from gpu_common import (REL_L2_TOL, REL_MAX_TOL, W_RTOL, bits_to_f64, moe_mod, out_bits, output_errors,
+                        run_forward, torch_cuda, upload, ws_for, ws_read, x_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def read_intermediates(dl, ws, rows):
+    moe = moe_mod()
+    L = moe.moe_workspace_layout(dl.cfg)
+    k, h = dl.cfg.top_k, dl.cfg.hidden
+    imax = max(dl.cfg.moe_inter, dl.cfg.shared_inter)
+    U = int(ws_read(ws, L.union_count, np.int32, 1)[0])
+    return dict(
+        ids=ws_read(ws, L.topk_ids, np.int32, 8 * k).reshape(8, k)[:rows],
+        weights=ws_read(ws, L.topk_w, np.float32, 8 * k).reshape(8, k)[:rows],
+        gamma=ws_read(ws, L.gamma, np.float32, 8)[:rows],
+        union_count=U,
+        union_ids=ws_read(ws, L.union_ids, np.int32, 64)[:U],
+        slot_to_union=ws_read(ws, L.slot_to_union, np.int32, rows * k),
+        row_mask=ws_read(ws, L.row_mask, np.uint32, 64)[:U],
+        act=ws_read(ws, L.act, np.uint16, 65 * 8 * imax).reshape(65, 8, imax),
+        y=ws_read(ws, L.y, np.float32, 65 * 8 * h).reshape(65, 8, h),
+    )
+
+
+def check_against_oracle(weights, dl, x_bits, rows_checked=None):
+    R = x_bits.shape[0]
+    got, ws = run_forward(dl, x_bits)
+    ref = moe_layer_from(weights, x_bits, rows=rows_checked)
+    mid = read_intermediates(dl, ws, R)
+    assert np.array_equal(mid["ids"], ref["ids"])
+    np.testing.assert_allclose(mid["weights"], ref["weights"], rtol=W_RTOL, atol=0)
+    assert mid["union_count"] == ref["union_count"]
+    assert np.array_equal(mid["union_ids"], ref["union_ids"])
+    assert np.array_equal(mid["slot_to_union"], ref["slot_to_union"])
+    assert np.array_equal(mid["row_mask"], ref["row_mask"])
+    rows = ref["rows"]
+    rel_l2, rel_max = output_errors(got[rows], ref["out"][rows])
+    assert np.all(rel_l2 <= REL_L2_TOL), rel_l2
+    assert np.all(rel_max <= REL_MAX_TOL), rel_max
+    # expert outputs y per (row, slot) and the shared expert
+    for r in rows:
+        for j in range(dl.cfg.top_k):
+            u = ref["slot_to_union"][r * dl.cfg.top_k + j]
+            yr = ref["y"][r, j].astype(np.float64)
+            yg = mid["y"][u, r].astype(np.float64)
+            assert np.linalg.norm(yg - yr) <= 1e-2 * np.linalg.norm(yr)
+        sr = ref["shared_y"][r].astype(np.float64)
+        assert np.linalg.norm(mid["y"][64, r] - sr) <= 1e-2 * np.linalg.norm(sr)
+    return got, ref, rel_l2
+
+
+@pytest.mark.parametrize("name", ["c0_tiny", "c1_e64_decode", "c2_e128_verify2"])
+def test_forward_small_configs(name):
+    shape = synth.CONFIGS[name]
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    for step in range(2):
+        _, _, rel = check_against_oracle(weights, dl, synth.activations(shape, step))
+        print(name, "step", step, "rel_l2", rel)
+
+
+@pytest.fixture(scope="module")
+def layer256():
+    shape = synth.CONFIGS["c4_e256_prefill8"]
+    weights = synth.layer_weights(shape, materialise=True, threads=16)
+    dl = upload(weights)
+    weights._experts.clear()  # host copies no longer needed; the oracle regenerates experts
+    weights.lazy = True
+    return weights, dl
+
+
+def test_forward_c3_verify4_full(layer256):
+    weights, dl = layer256
+    shape = synth.CONFIGS["c3_e256_verify4"]
+    w3 = dataclasses.replace(weights, shape=shape)  # same weights: c3 and c4 share shape and seed
+    check_against_oracle(w3, dl, synth.activations(shape, 0))
+
+
+def test_forward_c4_prefill8_sampled_rows(layer256):
+    weights, dl = layer256
+    shape = synth.CONFIGS["c4_e256_prefill8"]
+    check_against_oracle(weights, dl, synth.activations(shape, 0), rows_checked=[0, 7])
+
+
+def test_rows_equal_one_row_calls_256(layer256):
+    weights, dl = layer256
+    shape = synth.CONFIGS["c4_e256_prefill8"]
+    x = synth.activations(shape, 3)
+    singles = np.stack([run_forward(dl, x[r:r + 1])[0][0] for r in range(8)])
+    for R in range(1, 9):
+        got, _ = run_forward(dl, x[:R])
+        assert np.array_equal(got, singles[:R]), f"rows={R}"
+
+
+def test_deterministic_256(layer256):
+    _, dl = layer256
+    x = synth.activations(synth.CONFIGS["c4_e256_prefill8"], 5)
+    a, wa = run_forward(dl, x)
+    b, wb = run_forward(dl, x)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- crafted scales
+ALL_FINITE_E4M3 = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+
+
+def crafted_layer(shape, seed=1):
+    """Random codes; block scales drawn uniformly from every finite E4M3FN byte
+    (both signs, subnormals, 448); scale2 values other than 1."""
+    weights = synth.layer_weights(shape)
+    rng = np.random.default_rng(seed)
+
+    def craft(t, key):
+        r = np.random.default_rng([seed, *key])
+        return synth.Nvfp4Tensor(t.n, t.k, t.packed, r.choice(ALL_FINITE_E4M3, size=t.scales.shape),
+                                 float(r.choice([1.0, 0.5, 1.25])))
+
+    experts = {(e, p): craft(weights.expert(e, p), (e, p)) for e in range(shape.num_experts) for p in range(3)}
+    weights._experts = experts
+    weights.lazy = False
+    weights.shared = tuple(craft(t, (999, p)) for p, t in enumerate(weights.shared))
+    return weights
+
+
+def test_stages_with_every_scale_byte():
+    shape = synth.MoeShape("scales", 512, 8, 2, 256, 128, 3, synth.ROUTE_SOFTMAX, True, 1.0)
+    weights = crafted_layer(shape)
+    dl = upload(weights)
+    x = synth.activations(shape, 0)
+    got, ws = run_forward(dl, x)
+    mid = read_intermediates(dl, ws, shape.rows)
+    xf = bits_to_f64(x)
+    U = mid["union_count"]
+    slots = list(range(U)) + [64]
+    for u in slots:
+        if u == 64:
+            g, up, dn = weights.shared
+            mask = (1 << shape.rows) - 1
+        else:
+            e = int(mid["union_ids"][u])
+            g, up, dn = (weights.expert(e, p) for p in range(3))
+            mask = int(mid["row_mask"][u])
+        Wg, Wu, Wd = (dequant_nvfp4(t.packed, t.scales, t.scale2, t.n, t.k) for t in (g, up, dn))
+        for r in range(shape.rows):
+            if not (mask >> r) & 1:
+                continue
+            # gate/up: act = bf16(silu(g) * v) from float64 dot products
+            gd, vd = Wg @ xf[r], Wu @ xf[r]
+            gb = np.abs(Wg) @ np.abs(xf[r])
+            vb = np.abs(Wu) @ np.abs(xf[r])
+            act_g = bits_to_f64(mid["act"][u, r, :g.n])
+            a_ref = silu(gd) * vd
+            # bound: fp32 sums (relative 4e-6 of the absolute sums) propagated through silu(g)*v,
+            # plus one bf16 rounding of the result
+            dsilu = np.abs(silu(gd) / np.where(gd == 0, 1, gd)) + 1.0
+            bound = 4e-6 * (dsilu * gb * np.abs(vd) + np.abs(silu(gd)) * vb) + 2.0 ** -8 * np.abs(a_ref) + 1e-30
+            assert np.all(np.abs(act_g - a_ref) <= bound), (u, r)
+            # down: from the kernel's own bf16 activations
+            yd = Wd @ act_g
+            yb = np.abs(Wd) @ np.abs(act_g)
+            y_g = mid["y"][u, r].astype(np.float64)
+            assert np.all(np.abs(y_g - yd) <= 4e-6 * yb + 1e-30), (u, r)
+    ref = moe_layer_from(weights, x)
+    rel_l2, rel_max = output_errors(got, ref["out"])
+    assert np.all(rel_l2 <= REL_L2_TOL) and np.all(rel_max <= REL_MAX_TOL), (rel_l2, rel_max)
+
+
+# ---------------------------------------------------------------- shapes
+RAGGED = [
+    # h with a partial last chunk, tiny inter sizes, E = k, 64 ids, sigmoid without norm
+    synth.MoeShape("ragged_h", 2080, 12, 3, 96, 160, 5, synth.ROUTE_SIGMOID_BIAS, True, 2.5),
+    synth.MoeShape("k_eq_E", 256, 8, 8, 64, 32, 2, synth.ROUTE_SOFTMAX, True, 1.0),
+    synth.MoeShape("ids64", 1024, 96, 8, 128, 256, 8, synth.ROUTE_SIGMOID_BIAS, False, 1.5),
+    synth.MoeShape("soft_nonorm", 4160, 40, 6, 2080, 64, 4, synth.ROUTE_SOFTMAX, False, 1.0),
+    synth.MoeShape("k1", 128, 4, 1, 32, 32, 1, synth.ROUTE_SOFTMAX, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=[s.name for s in RAGGED])
+def test_ragged_and_edge_shapes(shape):
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = synth.activations(shape, 1)
+    check_against_oracle(weights, dl, x)
+    singles = np.stack([run_forward(dl, x[r:r + 1])[0][0] for r in range(shape.rows)])
+    got, _ = run_forward(dl, x)
+    assert np.array_equal(got, singles)
+
+
+def test_graph_capture_replays():
+    torch = torch_cuda()
+    moe = moe_mod()
+    shape = synth.CONFIGS["c2_e128_verify2"]
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    xs = [synth.activations(shape, s) for s in range(3)]
+    eager = [run_forward(dl, x)[0] for x in xs]
+    x = x_dev(xs[0])
+    out = torch.zeros_like(x)
+    ws = ws_for(dl.cfg)
+    moe.moe_forward(dl.cfg, dl.weights, x, out, ws)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_forward(dl.cfg, dl.weights, x, out, ws)
+    for rep in range(6):
+        x.copy_(x_dev(xs[rep % 3]))
+        out.zero_()
+        _ = torch.ones(1 << 20, device="cuda").sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out_bits(out), eager[rep % 3]), rep
