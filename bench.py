@@ -30,9 +30,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "routed-MoE layer µs/step + achieved HBM GB/s (% peak), rows=1..8, NVFP4"
+
+# HBM bytes per dispatch of the gate/up sweep at rows=8, measured with rocprofv3 --pmc
+# (FETCH_SIZE x 2.000 + WRITE_SIZE; the factor comes from a plain 1 GiB copy, see
+# profiles/moe_forward_e256_rows8_pmc.md).  Valid only for the kernel sources it was taken on.
+TRAFFIC_SOURCES = ("mixture_experts_decode_gate_amd/csrc/moe_kernels.hip",
+                   "mixture_experts_decode_gate_amd/csrc/moe_device.h")
+TRAFFIC_MEASURED = {"sources_sha256_16": "076a4f87f560a97d", "rows": 8, "gate_up_sweep_bytes": 790_504_000}
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "c4_e256_prefill8"
 N_INPUTS = 16
+
+
+def measured_traffic(rows: int):
+    """Counter-measured bytes per launch of the dominant kernel, or None when the
+    kernel sources changed since the counters were taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != TRAFFIC_MEASURED["sources_sha256_16"] or rows != TRAFFIC_MEASURED["rows"]:
+        return None
+    return TRAFFIC_MEASURED["gate_up_sweep_bytes"]
 
 
 def log(*a):
@@ -90,7 +110,12 @@ def union_sizes(cfg, layer, xs, ws):
     return us
 
 
-def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, with_stage_events=True):
+def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, event_every=0):
+    """K back-to-back steps between two events on the launch stream.  With
+    event_every > 0, every event_every-th step is launched through
+    moe_forward_timed, which records an event before and after each stage of
+    that step on the same stream (stage durations for the roofline); the other
+    steps run moe_forward unchanged."""
     import torch
     import mixture_experts_decode_gate_amd as moe
     from mixture_experts_decode_gate_amd.hip_events import HipEvent
@@ -100,14 +125,15 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, with_stage_ev
     nst = moe.moe_num_stages()
     for i in range(warmup):
         moe.moe_forward(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], out, ws)
-    events = [[HipEvent() for _ in range(nst + 1)] for _ in range(steps)] if with_stage_events else None
+    traced = [i for i in range(steps) if event_every and i % event_every == 0]
+    events = {i: [HipEvent() for _ in range(nst + 1)] for i in traced}
     start, end = HipEvent(), HipEvent()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(sh)
     for i in range(steps):
         lay, xi = layers[i % len(layers)], i % len(xs)
-        if with_stage_events:
+        if i in events:
             moe.moe_forward_timed(cfg, lay.weights, xs[xi], out, ws, events[i])
         else:
             moe.moe_forward(cfg, lay.weights, xs[xi], out, ws)
@@ -120,14 +146,14 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, with_stage_ev
                layer_bytes=sum(b["layer"] for b in sbytes),
                mean_union=float(np.mean([us[i % len(xs)] for i in range(steps)])))
     res["gbps"] = res["layer_bytes"] / (total_ms * 1e-3) / 1e9
-    if with_stage_events:
+    if traced:
         names = moe.moe_stage_names()
         stage = {}
         for s, name in enumerate(names):
-            d = [events[i][s].elapsed_ms(events[i][s + 1]) for i in range(steps)]
-            b = sum(sb[name] for sb in sbytes)
+            d = [events[i][s].elapsed_ms(events[i][s + 1]) for i in traced]
+            b = sum(sbytes[i][name] for i in traced)
             stage[name] = dict(avg_us=float(np.mean(d)) * 1e3, gbps=b / (sum(d) * 1e-3) / 1e9,
-                               bytes_per_launch=b / steps)
+                               bytes_per_launch=b / len(traced), launches=len(traced))
         res["stages"] = stage
     return res
 
@@ -189,6 +215,8 @@ def main():
     ap.add_argument("--rows", type=int, default=8)
     ap.add_argument("--layers", type=int, default=8, help="device copies of the layer cycled by the steps")
     ap.add_argument("--sweep-steps", type=int, default=100)
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="record per-stage events on every n-th timed step (0: none)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for rocprofv3: no sweep, no CPU leg")
@@ -227,7 +255,8 @@ def main():
     xs = inputs(args.rows)
     us = union_sizes(cfg, layers[0], xs, ws)
     log(f"[bench] unions over {N_INPUTS} inputs: {us}")
-    res = timed_run(cfg, layers, xs, us, shape, args.rows, args.steps, args.warmup, ws)
+    res = timed_run(cfg, layers, xs, us, shape, args.rows, args.steps, args.warmup, ws,
+                    event_every=args.event_every)
     log(f"[bench] rows={args.rows}: {res['us_per_step']:.1f} us/step, {res['gbps']:.0f} GB/s")
 
     sweep = []
@@ -235,8 +264,7 @@ def main():
         for R in range(1, 9):
             xr = inputs(R)
             ur = union_sizes(cfg, layers[0], xr, ws)
-            r = timed_run(cfg, layers, xr, ur, base_shape.with_rows(R), R, args.sweep_steps, 10, ws,
-                          with_stage_events=False)
+            r = timed_run(cfg, layers, xr, ur, base_shape.with_rows(R), R, args.sweep_steps, 10, ws)
             sweep.append(dict(rows=R, us_per_step=round(r["us_per_step"], 2), gbps=round(r["gbps"], 1),
                               frac=round(r["gbps"] / HBM_PEAK_GBPS, 4), mean_union=r["mean_union"]))
             log(f"[bench] sweep rows={R}: {r['us_per_step']:.1f} us/step {r['gbps']:.0f} GB/s U={r['mean_union']:.2f}")
@@ -269,8 +297,10 @@ def main():
                    "rows": args.rows, "layer_copies": args.layers, "inputs": N_INPUTS,
                    "mean_union": res["mean_union"]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(st["gbps"], 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(st["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "avg_launch_us": round(st["avg_us"], 2), "bytes_per_launch": int(st["bytes_per_launch"])},
+                     "unit": "GB/s", "frac": round(st["gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(args.rows),
+                     "avg_launch_us": round(st["avg_us"], 2), "bytes_per_launch": int(st["bytes_per_launch"]),
+                     "timed_launches": st["launches"]},
         "stages_us": {k: round(v["avg_us"], 2) for k, v in res["stages"].items()},
         "copy_gbps": round(copy_gbps, 1),
         "sweep": sweep,

@@ -84,7 +84,8 @@ enum {
   MOE_MAX_ROWS = 8,           /* rows per call ("WIDENED (2026-08-31)" note)     */
   MOE_MAX_IDS = 64,           /* top_k * rows ("RETRACTED (2026-08-29)" note)    */
   MOE_MAX_EXPERTS = 1024,     /* design cap on num_experts                       */
-  MOE_MAX_DIM = 8192,         /* cap on hidden, moe_inter and shared_inter       */
+  MOE_MAX_DIM = 8192,         /* cap on hidden                                   */
+  MOE_MAX_INTER = 4096,       /* cap on moe_inter and shared_inter               */
   MOE_DIM_ALIGN = 32          /* hidden, moe_inter, shared_inter multiple of 32  */
 };
 
@@ -134,7 +135,6 @@ typedef struct moe_weights {
  * The layout depends on the config only (sized for MOE_MAX_ROWS rows).
  * Offsets are multiples of 256. */
 typedef struct moe_ws_layout {
-  size_t partials;      /* double [nkc][MOE_MAX_ROWS][E+1] router K-chunk partial dots */
   size_t logits;        /* float  [MOE_MAX_ROWS][E]   router logits (row stride E)    */
   size_t gamma;         /* float  [MOE_MAX_ROWS]      sigmoid(x_r . shared gate)      */
   size_t topk_ids;      /* int32  [MOE_MAX_ROWS][k]   (row stride k)                  */
@@ -162,7 +162,7 @@ moe_status moe_workspace_layout(const moe_config* cfg, moe_ws_layout* out);
  *   x_bf16    [rows, h] bf16 bits, 16-byte aligned
  *   topk_ids  [rows, k] int32 out, ordered by descending key, ties by lower id
  *   topk_w    [rows, k] fp32 out
- * Also leaves partials, logits and gamma in the workspace. */
+ * Also leaves logits and gamma in the workspace. */
 moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                      int32_t rows, int32_t* topk_ids, float* topk_w,
                      void* ws, size_t ws_bytes, void* stream);

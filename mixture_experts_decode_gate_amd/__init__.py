@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID_BIAS = 0, 1
-MOE_MAX_ROWS, MOE_MAX_IDS, MOE_MAX_EXPERTS, MOE_MAX_DIM = 8, 64, 1024, 8192
+MOE_MAX_ROWS, MOE_MAX_IDS, MOE_MAX_EXPERTS, MOE_MAX_DIM, MOE_MAX_INTER = 8, 64, 1024, 8192, 4096
 SHARED_SLOT = MOE_MAX_IDS
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
@@ -70,7 +70,7 @@ class MoeWeights(ctypes.Structure):
 
 class MoeWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "partials", "logits", "gamma", "topk_ids", "topk_w", "union_ids", "union_count", "slot_to_union",
+        "logits", "gamma", "topk_ids", "topk_w", "union_ids", "union_count", "slot_to_union",
         "row_mask", "slot_info", "act", "y", "total")]
 
 

@@ -50,12 +50,12 @@ moe_status check_config(const moe_config* c) {
   if (c->hidden < MOE_DIM_ALIGN || c->hidden > MOE_MAX_DIM || c->hidden % MOE_DIM_ALIGN)
     return fail(MOE_ERR_INVALID_ARG, "hidden=%d must be a multiple of %d in [%d, %d]", c->hidden, MOE_DIM_ALIGN,
                 MOE_DIM_ALIGN, MOE_MAX_DIM);
-  if (c->moe_inter < MOE_DIM_ALIGN || c->moe_inter > MOE_MAX_DIM || c->moe_inter % MOE_DIM_ALIGN)
+  if (c->moe_inter < MOE_DIM_ALIGN || c->moe_inter > MOE_MAX_INTER || c->moe_inter % MOE_DIM_ALIGN)
     return fail(MOE_ERR_INVALID_ARG, "moe_inter=%d must be a multiple of %d in [%d, %d]", c->moe_inter,
-                MOE_DIM_ALIGN, MOE_DIM_ALIGN, MOE_MAX_DIM);
-  if (c->shared_inter < MOE_DIM_ALIGN || c->shared_inter > MOE_MAX_DIM || c->shared_inter % MOE_DIM_ALIGN)
+                MOE_DIM_ALIGN, MOE_DIM_ALIGN, MOE_MAX_INTER);
+  if (c->shared_inter < MOE_DIM_ALIGN || c->shared_inter > MOE_MAX_INTER || c->shared_inter % MOE_DIM_ALIGN)
     return fail(MOE_ERR_INVALID_ARG, "shared_inter=%d must be a multiple of %d in [%d, %d]", c->shared_inter,
-                MOE_DIM_ALIGN, MOE_DIM_ALIGN, MOE_MAX_DIM);
+                MOE_DIM_ALIGN, MOE_DIM_ALIGN, MOE_MAX_INTER);
   if (c->num_experts < 1 || c->num_experts > MOE_MAX_EXPERTS)
     return fail(MOE_ERR_INVALID_ARG, "num_experts=%d outside [1, %d]", c->num_experts, MOE_MAX_EXPERTS);
   if (c->top_k < 1 || c->top_k > c->num_experts || c->top_k > MOE_MAX_IDS)
@@ -126,7 +126,6 @@ moe_status check_all_weights(const moe_config* c, const moe_weights* w) {
 
 void compute_layout(const moe_config* c, moe_ws_layout* L) {
   const size_t R = MOE_MAX_ROWS, E = (size_t)c->num_experts, k = (size_t)c->top_k, h = (size_t)c->hidden;
-  const size_t nkc = (h + 2047) / 2048;
   const size_t imax = (size_t)(c->moe_inter > c->shared_inter ? c->moe_inter : c->shared_inter);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -134,7 +133,6 @@ void compute_layout(const moe_config* c, moe_ws_layout* L) {
     off = round_up(off + bytes, 256);
     return o;
   };
-  L->partials = take(nkc * R * (E + 1) * sizeof(double));
   L->logits = take(R * E * sizeof(float));
   L->gamma = take(R * sizeof(float));
   L->topk_ids = take(R * k * sizeof(int32_t));
@@ -179,8 +177,6 @@ moe_status device_status(hipError_t e, const char* what) {
 void fill_topk(moe::TopkParams& p, const moe_config* c, const moe_weights* w, int32_t rows, char* ws,
                const moe_ws_layout& L, int32_t* ids_out, float* w_out) {
   memset(&p, 0, sizeof p);
-  p.partials = reinterpret_cast<const double*>(ws + L.partials);
-  p.nkc = (c->hidden + 2047) / 2048;
   p.bias = w->correction_bias;
   p.E = c->num_experts;
   p.k = c->top_k;
@@ -188,8 +184,7 @@ void fill_topk(moe::TopkParams& p, const moe_config* c, const moe_weights* w, in
   p.route_kind = c->route_kind;
   p.norm = c->norm_topk_prob;
   p.rsf = c->routed_scaling_factor;
-  p.logits = reinterpret_cast<float*>(ws + L.logits);
-  p.gamma = reinterpret_cast<float*>(ws + L.gamma);
+  p.logits = reinterpret_cast<const float*>(ws + L.logits);
   p.ids_out = ids_out;
   p.w_out = w_out;
   p.union_ids = reinterpret_cast<int32_t*>(ws + L.union_ids);
@@ -244,8 +239,8 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
 
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return device_status(e, "event record");
-  e = moe::launch_router(x, w->router_w, w->shared_expert_gate, reinterpret_cast<double*>(wsb + L.partials),
-                         rows, cfg->hidden, cfg->num_experts, s);
+  e = moe::launch_router(x, w->router_w, w->shared_expert_gate, reinterpret_cast<float*>(wsb + L.logits),
+                         reinterpret_cast<float*>(wsb + L.gamma), rows, cfg->hidden, cfg->num_experts, s);
   if (e != hipSuccess) return device_status(e, "router launch");
   if ((e = mark(1)) != hipSuccess) return device_status(e, "event record");
   if ((e = moe::launch_topk(tp, true, s)) != hipSuccess) return device_status(e, "top-k launch");
@@ -254,7 +249,8 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
   if ((e = mark(3)) != hipSuccess) return device_status(e, "event record");
   if ((e = moe::launch_down(sp, rows, max_union, s)) != hipSuccess) return device_status(e, "down launch");
   if ((e = mark(4)) != hipSuccess) return device_status(e, "event record");
-  e = moe::launch_blend(sp.y, wts, tp.slot_to_union, tp.gamma, out, rows, cfg->hidden, cfg->top_k, s);
+  e = moe::launch_blend(sp.y, wts, tp.slot_to_union, reinterpret_cast<const float*>(wsb + L.gamma), out, rows,
+                        cfg->hidden, cfg->top_k, s);
   if (e != hipSuccess) return device_status(e, "blend launch");
   if ((e = mark(5)) != hipSuccess) return device_status(e, "event record");
   return ok();
@@ -299,8 +295,8 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t
   moe::TopkParams tp;
   fill_topk(tp, cfg, w, rows, wsb, L, topk_ids, topk_w);
   hipError_t e = moe::launch_router(x_bf16, w->router_w, w->shared_expert_gate,
-                                    reinterpret_cast<double*>(wsb + L.partials), rows, cfg->hidden,
-                                    cfg->num_experts, s);
+                                    reinterpret_cast<float*>(wsb + L.logits), reinterpret_cast<float*>(wsb + L.gamma),
+                                    rows, cfg->hidden, cfg->num_experts, s);
   if (e != hipSuccess) return device_status(e, "router launch");
   if ((e = moe::launch_topk(tp, false, s)) != hipSuccess) return device_status(e, "top-k launch");
   return ok();

@@ -62,18 +62,101 @@ __device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
 }
 
-// Butterfly sum over the 64 lanes.  Lanes may differ in the last bit; callers
-// take lane 0's value so the result is deterministic.
+// DPP lane move: lanes outside ROW_MASK read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)src, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Sum over the 64 lanes with DPP: pairs, quads, half rows, rows (16 lanes),
+// then row 1 += row 0 and row 3 += row 2 (row_bcast:15), and rows 2-3 +=
+// lane 31 (row_bcast:31).  Lane 63 ends with the total, which is returned to
+// every lane.  The order of additions is fixed, so the result is
+// deterministic.
 __device__ __forceinline__ float wave_sum(float v) {
+  v += __builtin_bit_cast(float, dpp_u32<0xB1, 0xF>(__builtin_bit_cast(uint32_t, v)));   // quad_perm [1,0,3,2]
+  v += __builtin_bit_cast(float, dpp_u32<0x4E, 0xF>(__builtin_bit_cast(uint32_t, v)));   // quad_perm [2,3,0,1]
+  v += __builtin_bit_cast(float, dpp_u32<0x141, 0xF>(__builtin_bit_cast(uint32_t, v)));  // row_half_mirror
+  v += __builtin_bit_cast(float, dpp_u32<0x140, 0xF>(__builtin_bit_cast(uint32_t, v)));  // row_mirror
+  v += __builtin_bit_cast(float, dpp_u32<0x142, 0xA>(__builtin_bit_cast(uint32_t, v)));  // row_bcast:15
+  v += __builtin_bit_cast(float, dpp_u32<0x143, 0xC>(__builtin_bit_cast(uint32_t, v)));  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// wave_sum of N independent values, step by step, so each DPP step of one
+// value fills the hazard slots of the others.  Same addition order as
+// wave_sum for every value.
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+#define MOE_SUM_STEP(CTRL, MASK)                                                                   \
+  _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] += __builtin_bit_cast(                        \
+      float, dpp_u32<CTRL, MASK>(__builtin_bit_cast(uint32_t, v[i])));
+  MOE_SUM_STEP(0xB1, 0xF)
+  MOE_SUM_STEP(0x4E, 0xF)
+  MOE_SUM_STEP(0x141, 0xF)
+  MOE_SUM_STEP(0x140, 0xF)
+  MOE_SUM_STEP(0x142, 0xA)
+  MOE_SUM_STEP(0x143, 0xC)
+#undef MOE_SUM_STEP
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  for (int i = 0; i < N; ++i) v[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[i]), 63));
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)b);
+  const uint64_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, (hi << 32) | lo);
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f64<0xB1, 0xF>(v);
+  v += dpp_f64<0x4E, 0xF>(v);
+  v += dpp_f64<0x141, 0xF>(v);
+  v += dpp_f64<0x140, 0xF>(v);
+  v += dpp_f64<0x142, 0xA>(v);
+  v += dpp_f64<0x143, 0xC>(v);
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+// Maximum over the 64 lanes (same DPP pattern as wave_sum), returned to every lane.
+__device__ __forceinline__ uint64_t wave_max(uint64_t v) {
+  auto step = [](uint64_t a, uint64_t o) { return o > a ? o : a; };
+#define MOE_DPP_MAX_STEP(CTRL, MASK)                                                   \
+  {                                                                                    \
+    const uint64_t lo = dpp_u32<CTRL, MASK>((uint32_t)v);                              \
+    const uint64_t hi = dpp_u32<CTRL, MASK>((uint32_t)(v >> 32));                      \
+    v = step(v, (hi << 32) | lo);                                                      \
+  }
+  MOE_DPP_MAX_STEP(0xB1, 0xF)
+  MOE_DPP_MAX_STEP(0x4E, 0xF)
+  MOE_DPP_MAX_STEP(0x141, 0xF)
+  MOE_DPP_MAX_STEP(0x140, 0xF)
+  MOE_DPP_MAX_STEP(0x142, 0xA)
+  MOE_DPP_MAX_STEP(0x143, 0xC)
+#undef MOE_DPP_MAX_STEP
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return (hi << 32) | lo;
+}
+
+// The wave's index within its block, as a scalar (wave-uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+typedef __attribute__((address_space(1))) const uint16_t global_u16;
+
+// Weight bytes are read once per call: non-temporal global loads keep them
+// from displacing reused data in the caches.
+__device__ __forceinline__ u32x4 ld_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load((global_u32x4*)p);
+}
+__device__ __forceinline__ uint32_t ld_stream_u16(const uint8_t* p) {
+  return __builtin_nontemporal_load((global_u16*)p);
 }
 
 // Decode 32 E2M1 codes (one 16-byte load) into 16 bf16 pairs, column order.

@@ -11,13 +11,10 @@ namespace moe {
 struct SlotInfo;
 
 struct TopkParams {
-  const double* partials;  // [nkc][8][E+1]
-  int nkc;
   const float* bias;       // [E] or null (softmax)
   int E, k, rows, route_kind, norm;
   float rsf;
-  float* logits;           // [8][E]
-  float* gamma;            // [8]
+  const float* logits;     // [8][E], written by the router kernel
   int32_t* ids_out;        // [rows][k]
   float* w_out;            // [rows][k]
   // union outputs (moe_forward only)
@@ -45,8 +42,8 @@ struct SweepParams {
 
 constexpr size_t kSlotInfoBytes = 72;  // sizeof(SlotInfo), checked in the kernels file
 
-hipError_t launch_router(const uint16_t* x, const float* router_w, const float* gate_vec, double* partials,
-                         int rows, int h, int E, hipStream_t s);
+hipError_t launch_router(const uint16_t* x, const float* router_w, const float* gate_vec, float* logits,
+                         float* gamma, int rows, int h, int E, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, bool with_union, hipStream_t s);
 hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids, int32_t* union_count,
                         int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);

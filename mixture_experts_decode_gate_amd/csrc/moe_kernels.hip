@@ -16,47 +16,72 @@
 // in an order that does not depend on the other rows, so a call with R rows
 // writes each row's output bytes exactly as a one-row call would.
 
+#include <stdlib.h>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------- router
-// One wave per (router row e, 2048-column chunk c).  e == E is the shared
-// expert's gate vector.  Each lane accumulates in fp64 over its columns; the
-// chunk partials are summed in chunk order by the top-k kernel.
+// One block per router row e (e == E is the shared expert's gate vector), one
+// wave per kRouterChunk-column chunk.  Every load of a wave is issued before
+// any arithmetic; each lane accumulates its columns in fp64, the wave reduces
+// in a fixed order, and the chunk partials are summed in chunk order and
+// rounded once: logits[r][e] = fp32(sum), gamma[r] = fp32(sigmoid(sum)).
+constexpr int kRouterChunk = 1024;
+constexpr int kMaxRouterChunks = MOE_MAX_DIM / kRouterChunk;
+
 template <int R>
-__global__ __launch_bounds__(256) void router_kernel(const uint16_t* __restrict__ x,
-                                                     const float* __restrict__ router_w,
-                                                     const float* __restrict__ gate_vec,
-                                                     double* __restrict__ partials, int h, int E) {
+__global__ __launch_bounds__(64 * kMaxRouterChunks) void router_kernel(const uint16_t* __restrict__ x,
+                                                                       const float* __restrict__ router_w,
+                                                                       const float* __restrict__ gate_vec,
+                                                                       float* __restrict__ logits,
+                                                                       float* __restrict__ gamma, int h, int E) {
+  __shared__ double part[kMaxRouterChunks][kMaxRows];
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int c = blockIdx.y;
-  if (e > E) return;
+  const int c = wave_id();
+  const int nkc = blockDim.x >> 6;
+  const int e = blockIdx.x;
   const float* row = (e < E) ? router_w + (size_t)e * h : gate_vec;
-  double acc[R];
+  constexpr int kIt = kRouterChunk / 256;
+  float4 wv[kIt];
+  uint2 xv[R][kIt];
+  bool ok[kIt];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0;
-#pragma unroll 2
-  for (int it = 0; it < kChunk / 256; ++it) {
-    const int col = c * kChunk + it * 256 + lane * 4;
-    if (col < h) {
-      const float4 wv = *reinterpret_cast<const float4*>(row + col);
+  for (int it = 0; it < kIt; ++it) {
+    const int col = c * kRouterChunk + it * 256 + lane * 4;
+    ok[it] = col < h;
+    const int cc = ok[it] ? col : h - 4;  // in-bounds; the contribution is dropped below
+    const u32x4 w4 = ld_stream(reinterpret_cast<const uint8_t*>(row + cc));
+    wv[it] = make_float4(__uint_as_float(w4.x), __uint_as_float(w4.y), __uint_as_float(w4.z), __uint_as_float(w4.w));
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)r * h + col);
-        acc[r] = __builtin_fma((double)bf16_to_f32(xv.x & 0xFFFFu), (double)wv.x, acc[r]);
-        acc[r] = __builtin_fma((double)bf16_to_f32(xv.x >> 16), (double)wv.y, acc[r]);
-        acc[r] = __builtin_fma((double)bf16_to_f32(xv.y & 0xFFFFu), (double)wv.z, acc[r]);
-        acc[r] = __builtin_fma((double)bf16_to_f32(xv.y >> 16), (double)wv.w, acc[r]);
-      }
-    }
+    for (int r = 0; r < R; ++r) xv[r][it] = *reinterpret_cast<const uint2*>(x + (size_t)r * h + cc);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const double s = wave_sum(acc[r]);
-    if (lane == 0) partials[((size_t)c * kMaxRows + r) * (E + 1) + e] = s;
+    double acc = 0.0;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const double w0 = ok[it] ? (double)wv[it].x : 0.0, w1 = ok[it] ? (double)wv[it].y : 0.0;
+      const double w2 = ok[it] ? (double)wv[it].z : 0.0, w3 = ok[it] ? (double)wv[it].w : 0.0;
+      acc = __builtin_fma((double)bf16_to_f32(xv[r][it].x & 0xFFFFu), w0, acc);
+      acc = __builtin_fma((double)bf16_to_f32(xv[r][it].x >> 16), w1, acc);
+      acc = __builtin_fma((double)bf16_to_f32(xv[r][it].y & 0xFFFFu), w2, acc);
+      acc = __builtin_fma((double)bf16_to_f32(xv[r][it].y >> 16), w3, acc);
+    }
+    const double s = wave_sum(acc);
+    if (lane == 0) part[c][r] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < R) {
+    const int r = threadIdx.x;
+    double z = 0.0;
+    for (int cc = 0; cc < nkc; ++cc) z += part[cc][r];
+    if (e < E)
+      logits[r * E + e] = (float)z;
+    else
+      gamma[r] = (float)(1.0 / (1.0 + exp(-z)));
   }
 }
 
@@ -72,11 +97,14 @@ __device__ void union_wave(const int32_t* ids_lds, int n, int k, int lane, int32
   uint32_t mask = 0;
   int row = 0, col = 0;
   for (int t = 0; t < n; ++t) {
-    const int v = ids_lds[t];
+    const int v = __builtin_amdgcn_readlane(id, t);  // slot t's id, broadcast
     const bool eq = (lane < n) && (v == id);
     if (eq && t < first) first = t;
     if (eq) mask |= 1u << row;
-    if (++col == k) { col = 0; ++row; }
+    if (++col == k) {
+      col = 0;
+      ++row;
+    }
   }
   const bool is_first = (lane < n) && (first == lane);
   const unsigned long long bal = __ballot(is_first);
@@ -127,11 +155,8 @@ __global__ __launch_bounds__(512) void topk_kernel(TopkParams p) {
       kv[i] = -__builtin_huge_valf();
       lv[i] = 0.f;
       selj[i] = -1;
-      if (e < E) {
-        double L = 0.0;
-        for (int c = 0; c < p.nkc; ++c) L += p.partials[((size_t)c * kMaxRows + r) * (E + 1) + e];
-        const float L32 = (float)L;
-        p.logits[r * E + e] = L32;
+      if (i * 64 < E && e < E) {
+        const float L32 = p.logits[r * E + e];
         lv[i] = L32;
         if (p.route_kind == MOE_ROUTE_SOFTMAX) {
           kv[i] = L32;
@@ -141,44 +166,41 @@ __global__ __launch_bounds__(512) void topk_kernel(TopkParams p) {
         }
       }
     }
-    if (lane == 0) {
-      double z = 0.0;
-      for (int c = 0; c < p.nkc; ++c) z += p.partials[((size_t)c * kMaxRows + r) * (E + 1) + E];
-      p.gamma[r] = (float)(1.0 / (1.0 + exp(-z)));
-    }
+    // Selection: the key maps to an order-preserving uint32 and packs with
+    // ~e into a uint64, so the wave maximum is the largest key, ties to the
+    // lower id.  Invalid or taken entries are 0.
     float top_logit = 0.f;
     for (int j = 0; j < k; ++j) {
-      float bk = -__builtin_huge_valf();
-      int be = 0x7FFFFFFF;
+      uint64_t best = 0;
 #pragma unroll
       for (int i = 0; i < kKeysPerLane; ++i) {
         const int e = lane + 64 * i;
-        if (e < E && selj[i] < 0 && kv[i] > bk) {
-          bk = kv[i];
-          be = e;
+        if (i * 64 < E && e < E && selj[i] < 0) {
+          uint32_t u = __float_as_uint(kv[i]);
+          u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+          const uint64_t pk = ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+          best = pk > best ? pk : best;
         }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ok = __shfl_xor(bk, o);
-        const int oe = __shfl_xor(be, o);
-        if (ok > bk || (ok == bk && oe < be)) {
-          bk = ok;
-          be = oe;
-        }
-      }
+      best = wave_max(best);
+      int be = (int)(0xFFFFFFFFu - (uint32_t)best);
       // NaN keys (outside the contract) can leave no winner; keep the id in
       // range so no later stage indexes the weight tables out of bounds.
-      if (be >= E) be = 0;
+      if (best == 0 || be >= E || be < 0) be = 0;
       if ((be & 63) == lane) {
 #pragma unroll
         for (int i = 0; i < kKeysPerLane; ++i)
           if (i == (be >> 6)) selj[i] = j;
       }
-      if (j == 0) top_logit = bk;  // softmax: the largest logit
       if (lane == 0) {
         p.ids_out[r * k + j] = be;
         s_ids[r * k + j] = be;
+      }
+      if (j == 0) {
+        // softmax: the largest logit is the first winner's logit (key == logit)
+        uint32_t u = (uint32_t)(best >> 32);
+        u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+        top_logit = __uint_as_float(u);
       }
     }
     // Weights.  Softmax: exp(L - max) normalised over all experts, or over the
@@ -262,9 +284,9 @@ __global__ __launch_bounds__(512) void topk_kernel(TopkParams p) {
 }
 
 // ---------------------------------------------------------------- sweeps
-// Stage R rows of a bf16 [R][cols] matrix (row stride `stride` elements) into
-// LDS as NCH chunks of 256 swizzled 16-byte units, zero beyond `cols`.  Only
-// rows in `mask` are staged.
+// Stage rows of a bf16 [rows][cols] matrix (row stride `stride` elements) into
+// LDS as NCH chunks of 256 swizzled 16-byte units per row, zero beyond
+// `cols`.  Only rows in `mask` are staged.
 template <int R, int NCH>
 __device__ __forceinline__ void stage_rows(u32x4* dst, const uint16_t* src, size_t stride, int cols,
                                            uint32_t mask) {
@@ -281,187 +303,336 @@ __device__ __forceinline__ void stage_rows(u32x4* dst, const uint16_t* src, size
   }
 }
 
-constexpr int kSweepThreads = 512;
-constexpr int kSweepWaves = kSweepThreads / 64;
-constexpr int kGateUpRowsPerWave = 2;
-constexpr int kGateUpTile = kSweepWaves * kGateUpRowsPerWave;  // gate/up rows per tile
-constexpr int kDownRowsPerWave = 8;
-constexpr int kDownTile = kSweepWaves * kDownRowsPerWave;      // output rows per tile
-
-// Gate+up sweep.  A tile is kGateUpTile consecutive rows n of one union
-// slot's gate and up matrices; each wave takes kGateUpRowsPerWave of them.
-// For each row n and each row r that uses the slot:
-//   act[slot][r][n] = bf16(silu(g) * v), g = W_gate[n,:] . x_r, v = W_up[n,:] . x_r.
-template <int R, int NCH>
-__global__ __launch_bounds__(kSweepThreads) void gateup_kernel(SweepParams p) {
-  extern __shared__ u32x4 xs[];  // [R][NCH][256] staged x rows
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int h = p.h;
-  stage_rows<R, NCH>(xs, p.x, (size_t)h, h, (1u << R) - 1u);
-  __syncthreads();
-
-  const int U = *p.union_count;
-  const int tpe_r = (p.inter + kGateUpTile - 1) / kGateUpTile;
-  const int tpe_s = (p.shared_inter + kGateUpTile - 1) / kGateUpTile;
-  const int ntiles = U * tpe_r + tpe_s;
-  const size_t code_stride = (size_t)h >> 1;
-  const size_t scale_stride = (size_t)h >> 4;
-
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    int slot, nb;
-    if (t < U * tpe_r) {
-      slot = t / tpe_r;
-      nb = t - slot * tpe_r;
-    } else {
-      slot = kSharedSlot;
-      nb = t - U * tpe_r;
-    }
-    const SlotInfo si = p.slots[slot];
-    const int n0 = nb * kGateUpTile + wave * kGateUpRowsPerWave;
-
-    // Issue every load of this wave's rows before any arithmetic.
-    u32x4 gq[kGateUpRowsPerWave][NCH], uq[kGateUpRowsPerWave][NCH];
-    uint32_t gsc[kGateUpRowsPerWave][NCH], usc[kGateUpRowsPerWave][NCH];
-#pragma unroll
-    for (int i = 0; i < kGateUpRowsPerWave; ++i) {
-      const int n = n0 + i;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int col = c * kChunk + lane * 32;
-        gq[i][c] = u32x4{0u, 0u, 0u, 0u};
-        uq[i][c] = u32x4{0u, 0u, 0u, 0u};
-        gsc[i][c] = 0u;
-        usc[i][c] = 0u;
-        if (n < si.inter && col < h) {
-          const size_t co = (size_t)n * code_stride + (col >> 1);
-          const size_t so = (size_t)n * scale_stride + (col >> 4);
-          gq[i][c] = *reinterpret_cast<const u32x4*>(si.gate_packed + co);
-          uq[i][c] = *reinterpret_cast<const u32x4*>(si.up_packed + co);
-          gsc[i][c] = *reinterpret_cast<const uint16_t*>(si.gate_scales + so);
-          usc[i][c] = *reinterpret_cast<const uint16_t*>(si.up_scales + so);
-        }
-      }
-    }
-
-#pragma unroll
-    for (int i = 0; i < kGateUpRowsPerWave; ++i) {
-      const int n = n0 + i;
-      if (n >= si.inter) break;
-      float ag[R], au[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        ag[r] = 0.f;
-        au[r] = 0.f;
-      }
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int col = c * kChunk + lane * 32;
-        if (col < h) {
-          bf16x2 gw[16], uw[16];
-          decode32(gq[i][c], gw);
-          decode32(uq[i][c], uw);
-          const float gs0 = e4m3<0>(gsc[i][c]), gs1 = e4m3<1>(gsc[i][c]);
-          const float us0 = e4m3<0>(usc[i][c]), us1 = e4m3<1>(usc[i][c]);
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            if ((si.row_mask >> r) & 1u) {
-              const u32x4* xr = xs + (r * NCH + c) * kChunkUnits;
-              const u32x4 x0 = xr[lane], x1 = xr[64 + lane], x2 = xr[128 + lane], x3 = xr[192 + lane];
-              ag[r] = dot32(gw, x0, x1, x2, x3, gs0, gs1, ag[r]);
-              au[r] = dot32(uw, x0, x1, x2, x3, us0, us1, au[r]);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if ((si.row_mask >> r) & 1u) {
-          const float g = wave_sum(ag[r]) * si.gate_scale2;
-          const float v = wave_sum(au[r]) * si.up_scale2;
-          if (lane == 0) {
-            const float a = g / (1.0f + __expf(-g)) * v;
-            p.act[((size_t)slot * kMaxRows + r) * p.act_stride + n] = f32_to_bf16(a);
-          }
-        }
-      }
-    }
+// Copy the slot table (routed slots [0, U) and the shared slot) into LDS.
+// Later reads come from LDS: a global load issued after the prefetched
+// weights would make the in-order load counter drain the prefetch.
+__device__ __forceinline__ void load_slot_table(SlotInfo* dst, const SlotInfo* src, int U) {
+  constexpr int kWords = (int)(sizeof(SlotInfo) / 4);
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
+  uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+  for (int i = threadIdx.x; i < kNumSlots * kWords; i += blockDim.x) {
+    const int slot = i / kWords;
+    if (slot < U || slot == kSharedSlot) d32[i] = s32[i];
   }
 }
 
-// Down sweep.  A tile is kDownTile consecutive output rows n of one union
-// slot's down matrix [h, inter]; the slot's act rows are staged in LDS.
-//   y[slot][r][n] = W_down[n,:] . act[slot][r][:]
+constexpr int kMaxSweepThreads = 512;
+
+// One row of a K-contiguous NVFP4 matrix as this lane sees it: NCH 16-byte
+// code loads (32 columns each, 2048 columns per chunk across the wave) and
+// the two E4M3 block scales of each.
+template <int NCH>
+struct RowRegs {
+  u32x4 q[NCH];
+  uint32_t s[NCH];
+};
+
+// Lanes whose columns lie past K load the row's last 32 columns instead (an
+// in-bounds, finite copy) and zero their two block scales, so they add
+// exactly 0 whatever the activations hold there.  No branch guards the loads
+// (a branch here makes the compiler drain the prefetched loads early).
+template <int NCH>
+__device__ __forceinline__ void load_row(RowRegs<NCH>& b, const uint8_t* packed, const uint8_t* scales, int n,
+                                         int K, int lane) {
+  const size_t co = (size_t)n * (size_t)(K >> 1);
+  const size_t so = (size_t)n * (size_t)(K >> 4);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int col = c * kChunk + lane * 32;
+    const uint32_t keep = col < K ? 0xFFFFu : 0u;
+    const int cc = col < K ? col : K - 32;
+    b.q[c] = ld_stream(packed + co + (cc >> 1));
+    b.s[c] = ld_stream_u16(scales + so + (cc >> 4)) & keep;
+  }
+}
+
+// Position in the flattened gate/up work list: union slot index (U means the
+// shared expert) and row n.  Advancing by a stride walks the routed slots'
+// I rows each, then the shared expert's Is rows.
+struct ItemCursor {
+  int su;  // 0..U-1 routed, U shared, > U done
+  int n;
+};
+
+__device__ __forceinline__ void advance(ItemCursor& c, int step, int U, int inter, int shared_inter) {
+  c.n += step;
+  while (c.su <= U) {
+    const int rows = c.su < U ? inter : shared_inter;
+    if (c.n < rows) break;
+    c.n -= rows;
+    ++c.su;
+  }
+}
+
+// Gate+up sweep.  Work items are rows n of each union slot's gate and up
+// matrices, dealt round-robin to every wave of the grid; a wave loads its next
+// item while it computes the current one.  For each row r that uses the slot:
+//   act[slot][r][n] = bf16(silu(g) * v), g = W_gate[n,:] . x_r, v = W_up[n,:] . x_r.
 template <int R, int NCH>
-__global__ __launch_bounds__(kSweepThreads) void down_kernel(SweepParams p) {
-  extern __shared__ u32x4 as_[];  // [R][NCH][256] staged act rows
+__global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p) {
+  extern __shared__ u32x4 xs[];  // [R][NCH][256] staged x rows
+  __shared__ SlotInfo s_slots[kNumSlots];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
   const int h = p.h;
   const int U = *p.union_count;
-  const int tpe = (h + kDownTile - 1) / kDownTile;
-  const int ntiles = (U + 1) * tpe;
+  stage_rows<R, NCH>(xs, p.x, (size_t)h, h, (1u << R) - 1u);
+  load_slot_table(s_slots, p.slots, U);
+  __syncthreads();
 
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int su = t / tpe;
-    const int nb = t - su * tpe;
-    const int slot = su < U ? su : kSharedSlot;
-    const SlotInfo si = p.slots[slot];
-    const int K = si.inter;
-    __syncthreads();  // the previous tile's LDS reads are done
-    stage_rows<R, NCH>(as_, p.act + (size_t)slot * kMaxRows * p.act_stride, (size_t)p.act_stride, K,
-                       si.row_mask);
-    __syncthreads();
+  const int W = gridDim.x * nwaves;
+  ItemCursor cur{0, 0};
+  advance(cur, blockIdx.x * nwaves + wave_id(), U, p.inter, p.shared_inter);
 
-    const size_t code_stride = (size_t)K >> 1;
-    const size_t scale_stride = (size_t)K >> 4;
-    const int n0 = nb * kDownTile + wave * kDownRowsPerWave;
-    u32x4 dq[kDownRowsPerWave][NCH];
-    uint32_t dsc[kDownRowsPerWave][NCH];
+  auto slot_of = [&](int su) { return su < U ? su : kSharedSlot; };
+  RowRegs<NCH> ga, ua, gb, ub;
+  SlotInfo sa, sb;
+  int na = 0, nb = 0, slot_a = 0, slot_b = 0;
+
+  auto fetch = [&](const ItemCursor& c, RowRegs<NCH>& g, RowRegs<NCH>& u, SlotInfo& si, int& n, int& slot) {
+    slot = slot_of(c.su);
+    si = s_slots[slot];
+    n = c.n;
+    load_row<NCH>(g, si.gate_packed, si.gate_scales, n, h, lane);
+    load_row<NCH>(u, si.up_packed, si.up_scales, n, h, lane);
+  };
+
+  auto compute = [&](const RowRegs<NCH>& g, const RowRegs<NCH>& u, const SlotInfo& si, int n, int slot) {
+    float ag[R], au[R];
 #pragma unroll
-    for (int i = 0; i < kDownRowsPerWave; ++i) {
-      const int n = n0 + i;
+    for (int r = 0; r < R; ++r) {
+      ag[r] = 0.f;
+      au[r] = 0.f;
+    }
+    // Lanes past the last column hold zero codes and scales, and the staged
+    // x is zero there too, so every lane runs the same code.
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int col = c * kChunk + lane * 32;
-        dq[i][c] = u32x4{0u, 0u, 0u, 0u};
-        dsc[i][c] = 0u;
-        if (n < h && col < K) {
-          dq[i][c] = *reinterpret_cast<const u32x4*>(si.down_packed + (size_t)n * code_stride + (col >> 1));
-          dsc[i][c] = *reinterpret_cast<const uint16_t*>(si.down_scales + (size_t)n * scale_stride + (col >> 4));
+    for (int c = 0; c < NCH; ++c) {
+      bf16x2 gw[16], uw[16];
+      decode32(g.q[c], gw);
+      decode32(u.q[c], uw);
+      const float gs0 = e4m3<0>(g.s[c]), gs1 = e4m3<1>(g.s[c]);
+      const float us0 = e4m3<0>(u.s[c]), us1 = e4m3<1>(u.s[c]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if ((si.row_mask >> r) & 1u) {
+          const u32x4* xr = xs + (r * NCH + c) * kChunkUnits;
+          const u32x4 x0 = xr[lane], x1 = xr[64 + lane], x2 = xr[128 + lane], x3 = xr[192 + lane];
+          ag[r] = dot32(gw, x0, x1, x2, x3, gs0, gs1, ag[r]);
+          au[r] = dot32(uw, x0, x1, x2, x3, us0, us1, au[r]);
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < kDownRowsPerWave; ++i) {
-      const int n = n0 + i;
-      if (n >= h) break;
-      float acc[R];
+    for (int r = 0; r < R; ++r) {
+      if ((si.row_mask >> r) & 1u) {
+        float gu[2] = {ag[r], au[r]};
+        wave_sum_n<2>(gu);
+        const float gv = gu[0] * si.gate_scale2;
+        const float uv = gu[1] * si.up_scale2;
+        if (lane == 0) {
+          const float a = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          p.act[((size_t)slot * kMaxRows + r) * p.act_stride + n] = f32_to_bf16(a);
+        }
+      }
+    }
+  };
+
+  if (cur.su > U) return;
+  // Loads of the next item are always issued (the current item again on the
+  // last step) so no branch separates them from the compute that overlaps them.
+  fetch(cur, ga, ua, sa, na, slot_a);
+  while (true) {
+    ItemCursor nxt = cur;
+    advance(nxt, W, U, p.inter, p.shared_inter);
+    const bool more = nxt.su <= U;
+    fetch(more ? nxt : cur, gb, ub, sb, nb, slot_b);
+    compute(ga, ua, sa, na, slot_a);
+    if (!more) break;
+    cur = nxt;
+    advance(nxt, W, U, p.inter, p.shared_inter);
+    const bool more2 = nxt.su <= U;
+    fetch(more2 ? nxt : cur, ga, ua, sa, na, slot_a);
+    compute(gb, ub, sb, nb, slot_b);
+    if (!more2) break;
+    cur = nxt;
+  }
+}
+
+// Down sweep.  The work is the row space of "segments": a segment is one
+// union slot and a group of up to kGroup of the rows that use it (a slot used
+// by more rows than that is swept once per group).  Every wave takes an equal
+// contiguous share of segments x h output rows -- at most two segments -- so
+// waves never wait for each other.  A wave holds its group's act rows in
+// registers (loaded once per segment) and loads its next batch of weight rows
+// while it computes the current batch.
+//   y[slot][r][n] = W_down[n,:] . act[slot][r][:]
+constexpr int kDownThreads = 256;
+constexpr int kDownBatch = 4;  // weight rows per prefetch batch (stored as float4s)
+
+template <int NCH>
+struct DownBatch {
+  RowRegs<NCH> row[kDownBatch];
+};
+
+template <int R, int NCH>
+__global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
+  constexpr int kGroup = NCH == 1 ? 4 : 2;
+  constexpr int kGroupsPerSlot = (kMaxRows + kGroup - 1) / kGroup;
+  constexpr int kMaxSegs = kNumSlots * kGroupsPerSlot;
+  __shared__ SlotInfo s_slots[kNumSlots];
+  __shared__ int s_seg_slot[kMaxSegs];
+  __shared__ uint32_t s_seg_rows[kMaxSegs];  // row i of the group in bits 4i..4i+3, count in bits 28..31
+  __shared__ int s_nseg;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int nwaves = blockDim.x >> 6;
+  const int h = p.h;
+  const int U = *p.union_count;
+  load_slot_table(s_slots, p.slots, U);
+  __syncthreads();
+  if (wave == 0) {
+    // Segments of routed slot su (lane su < U), in slot order, then the shared slot's.
+    uint32_t mask = lane < U ? s_slots[lane].row_mask : 0u;
+    const int cnt = __popc(mask);
+    const int groups = (cnt + kGroup - 1) / kGroup;
+    int incl = groups;  // inclusive prefix sum over lanes
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int seg = incl - groups;
+    for (int g = 0; g < groups; ++g) {
+      uint32_t packed = 0;
+      int n = 0;
+      for (int r = 0; r < kMaxRows && n < kGroup; ++r) {
+        if (((mask >> r) & 1u) && n >= 0) {
+          // skip the rows of earlier groups
+          if (__popc(mask & ((1u << r) - 1u)) >= g * kGroup) {
+            packed |= (uint32_t)r << (4 * n);
+            ++n;
+          }
+        }
+      }
+      s_seg_slot[seg + g] = lane;
+      s_seg_rows[seg + g] = packed | ((uint32_t)n << 28);
+    }
+    const int nrouted = __shfl(incl, 63);
+    if (lane == 0) {
+      int seg2 = nrouted;
+      for (int g = 0; g * kGroup < R; ++g) {
+        uint32_t packed = 0;
+        int n = 0;
+        for (int r = g * kGroup; r < R && n < kGroup; ++r, ++n) packed |= (uint32_t)r << (4 * n);
+        s_seg_slot[seg2] = kSharedSlot;
+        s_seg_rows[seg2] = packed | ((uint32_t)n << 28);
+        ++seg2;
+      }
+      s_nseg = seg2;
+    }
+  }
+  __syncthreads();
+
+  // Block b owns rows [N*b/B, N*(b+1)/B) of the segment row space; inside a
+  // segment its waves take interleaved batches of kDownBatch rows, so a block
+  // reads one contiguous window.
+  const long long N = (long long)s_nseg * h;
+  const long long b_begin = (N / kDownBatch) * blockIdx.x / gridDim.x * kDownBatch;
+  const long long b_end = (N / kDownBatch) * (blockIdx.x + 1) / gridDim.x * kDownBatch;
+
+  DownBatch<NCH> A, B;
+  u32x4 act[kGroup][NCH][4];
+  for (long long pos = b_begin; pos < b_end;) {
+    const int seg = (int)(pos / h);
+    const int n_begin = (int)(pos - (long long)seg * h);
+    const int n_end = (int)(((long long)seg + 1) * h < b_end ? h : b_end - (long long)seg * h);
+    pos += n_end - n_begin;
+    const int slot = s_seg_slot[seg];
+    const uint32_t rows = s_seg_rows[seg];
+    const int cnt = (int)(rows >> 28);
+    const SlotInfo& si = s_slots[slot];
+    const int K = si.inter;
+    const int stride = nwaves * kDownBatch;
+    int n0 = n_begin + wave * kDownBatch;
+    if (n0 >= n_end) continue;
+    // act rows of the group (unused entries repeat the last row).  Lanes past
+    // K read the row's first columns: finite values that meet zeroed scales.
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const int r = (int)((rows >> (4 * (i < cnt ? i : cnt - 1))) & 0xFu);
+      const uint16_t* src = p.act + ((size_t)slot * kMaxRows + r) * p.act_stride;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int col = c * kChunk + lane * 32;
-        if (col < K) {
-          bf16x2 dw[16];
-          decode32(dq[i][c], dw);
-          const float s0 = e4m3<0>(dsc[i][c]), s1 = e4m3<1>(dsc[i][c]);
+        const u32x4* q = reinterpret_cast<const u32x4*>(src + (col < K ? col : 0));
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            if ((si.row_mask >> r) & 1u) {
-              const u32x4* ar = as_ + (r * NCH + c) * kChunkUnits;
-              acc[r] = dot32(dw, ar[lane], ar[64 + lane], ar[128 + lane], ar[192 + lane], s0, s1, acc[r]);
+        for (int u = 0; u < 4; ++u) act[i][c][u] = q[u];
+      }
+    }
+    auto fetch = [&](int nb, DownBatch<NCH>& b) {
+#pragma unroll
+      for (int i = 0; i < kDownBatch; ++i) {
+        const int n = nb + i < n_end ? nb + i : n_end - 1;  // rows past the range are loaded, not computed
+        load_row<NCH>(b.row[i], si.down_packed, si.down_scales, n, K, lane);
+      }
+    };
+    // Rows of a batch: per group row, the batch's dot products are reduced
+    // together and written with 16-byte stores (batches start at multiples
+    // of 4 and h is a multiple of 32).
+    auto compute = [&](int nb, const DownBatch<NCH>& b) {
+      float acc[kGroup][kDownBatch];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+        for (int i = 0; i < kDownBatch; ++i) acc[g][i] = 0.f;
+#pragma unroll
+      for (int i = 0; i < kDownBatch; ++i) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          bf16x2 dw[16];
+          decode32(b.row[i].q[c], dw);
+          const float s0 = e4m3<0>(b.row[i].s[c]), s1 = e4m3<1>(b.row[i].s[c]);
+#pragma unroll
+          for (int g = 0; g < kGroup; ++g)
+            if (g < cnt)
+              acc[g][i] = dot32(dw, act[g][c][0], act[g][c][1], act[g][c][2], act[g][c][3], s0, s1, acc[g][i]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        if (g < cnt) {
+          wave_sum_n<kDownBatch>(acc[g]);
+          const int r = (int)((rows >> (4 * g)) & 0xFu);
+          float* dst = p.y + ((size_t)slot * kMaxRows + r) * h + nb;
+          if (lane == 0) {
+            const float d2 = si.down_scale2;
+#pragma unroll
+            for (int i = 0; i < kDownBatch; i += 4) {
+              if (nb + i + 4 <= n_end) {
+                *reinterpret_cast<float4*>(dst + i) =
+                    make_float4(acc[g][i] * d2, acc[g][i + 1] * d2, acc[g][i + 2] * d2, acc[g][i + 3] * d2);
+              } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  if (nb + i + q < n_end) dst[i + q] = acc[g][i + q] * d2;
+              }
             }
           }
         }
       }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if ((si.row_mask >> r) & 1u) {
-          const float yv = wave_sum(acc[r]) * si.down_scale2;
-          if (lane == 0) p.y[((size_t)slot * kMaxRows + r) * h + n] = yv;
-        }
-      }
+    };
+    fetch(n0, A);
+    while (true) {
+      const int n1 = n0 + stride;
+      fetch(n1 < n_end ? n1 : n0, B);
+      compute(n0, A);
+      if (n1 >= n_end) break;
+      const int n2 = n1 + stride;
+      fetch(n2 < n_end ? n2 : n1, A);
+      compute(n1, B);
+      if (n2 >= n_end) break;
+      n0 = n2;
     }
   }
 }
@@ -500,33 +671,50 @@ int cu_count() {
   return cached[dev];
 }
 
-// Persistent grid: every CU holds as many blocks as occupancy allows (queried
-// once per kernel instance), capped by the largest possible tile count.
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = atoi(v);
+  return x > 0 ? x : dflt;
+}
+
+// Sweep launch shape: threads per block and blocks per CU.  Blocks per CU is
+// the occupancy limit (queried once per kernel instance) capped so a CU runs
+// about kWavesPerCu waves; MOE_SWEEP_THREADS and MOE_WAVES_PER_CU override the
+// defaults for tuning runs.
+struct SweepShape {
+  int threads = 0;
+  int per_cu = 0;
+};
+
 template <typename K>
-int sweep_grid(K kernel, size_t lds, int max_tiles, int& per_cu_cache) {
-  if (per_cu_cache <= 0) {
+dim3 sweep_grid(K kernel, size_t lds, int max_blocks, SweepShape& cache, int default_threads) {
+  if (cache.threads <= 0) {
+    int threads = env_int("MOE_SWEEP_THREADS", default_threads);
+    if (threads > kMaxSweepThreads || threads % 64) threads = default_threads;
+    const int waves_per_cu = env_int("MOE_WAVES_PER_CU", 8);
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSweepThreads, lds) != hipSuccess ||
-        per_cu <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu <= 0)
       per_cu = 1;
-    per_cu_cache = per_cu;
+    const int want = (waves_per_cu * 64 + threads - 1) / threads;
+    cache.threads = threads;
+    cache.per_cu = per_cu < want ? per_cu : (want < 1 ? 1 : want);
   }
-  int grid = cu_count() * per_cu_cache;
-  if (grid > max_tiles) grid = max_tiles;
-  return grid < 1 ? 1 : grid;
+  int grid = cu_count() * cache.per_cu;
+  if (grid > max_blocks) grid = max_blocks;
+  return dim3(grid < 1 ? 1 : grid);
 }
 
 template <int R>
-hipError_t router_r(const uint16_t* x, const float* rw, const float* gv, double* partials, int h, int E,
+hipError_t router_r(const uint16_t* x, const float* rw, const float* gv, float* logits, float* gamma, int h, int E,
                     hipStream_t s) {
-  const int nkc = (h + kChunk - 1) / kChunk;
-  dim3 grid((E + 1 + 3) / 4, nkc);
-  hipLaunchKernelGGL((router_kernel<R>), grid, dim3(256), 0, s, x, rw, gv, partials, h, E);
+  const int nkc = (h + kRouterChunk - 1) / kRouterChunk;
+  hipLaunchKernelGGL((router_kernel<R>), dim3(E + 1), dim3(64 * nkc), 0, s, x, rw, gv, logits, gamma, h, E);
   return hipGetLastError();
 }
 
 template <int R, int NCH>
-hipError_t gateup_rn(const SweepParams& p, int max_tiles, hipStream_t s) {
+hipError_t gateup_rn(const SweepParams& p, int max_items, hipStream_t s) {
   const size_t lds = (size_t)R * NCH * kChunkUnits * 16;
   static bool attr_set = false;
   if (!attr_set) {
@@ -535,25 +723,29 @@ hipError_t gateup_rn(const SweepParams& p, int max_tiles, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  static int per_cu = 0;
-  const int grid = sweep_grid(gateup_kernel<R, NCH>, lds, max_tiles, per_cu);
-  hipLaunchKernelGGL((gateup_kernel<R, NCH>), dim3(grid), dim3(kSweepThreads), lds, s, p);
+  static SweepShape shape;
+  const dim3 grid = sweep_grid(gateup_kernel<R, NCH>, lds, 1 << 30, shape, 512);
+  const int waves = (int)grid.x * (shape.threads / 64);
+  dim3 g = grid;
+  if (waves > max_items) g.x = (max_items * 64 + shape.threads - 1) / shape.threads;
+  hipLaunchKernelGGL((gateup_kernel<R, NCH>), g, dim3(shape.threads), lds, s, p);
   return hipGetLastError();
 }
 
 template <int R, int NCH>
-hipError_t down_rn(const SweepParams& p, int max_tiles, hipStream_t s) {
-  const size_t lds = (size_t)R * NCH * kChunkUnits * 16;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e =
-        hipFuncSetAttribute((const void*)down_kernel<R, NCH>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+hipError_t down_rn(const SweepParams& p, int max_union, hipStream_t s) {
   static int per_cu = 0;
-  const int grid = sweep_grid(down_kernel<R, NCH>, lds, max_tiles, per_cu);
-  hipLaunchKernelGGL((down_kernel<R, NCH>), dim3(grid), dim3(kSweepThreads), lds, s, p);
+  if (per_cu <= 0) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, down_kernel<R, NCH>, kDownThreads, 0) != hipSuccess ||
+        occ <= 0)
+      occ = 1;
+    const int want = env_int("MOE_DOWN_WAVES_PER_CU", 12) / (kDownThreads / 64);
+    per_cu = occ < want ? occ : (want < 1 ? 1 : want);
+  }
+  const int grid = cu_count() * per_cu;
+  (void)max_union;
+  hipLaunchKernelGGL((down_kernel<R, NCH>), dim3(grid), dim3(kDownThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -569,29 +761,27 @@ hipError_t gateup_r(const SweepParams& p, int nch, int max_tiles, hipStream_t s)
 }
 
 template <int R>
-hipError_t down_r(const SweepParams& p, int nch, int max_tiles, hipStream_t s) {
+hipError_t down_r(const SweepParams& p, int nch, int max_union, hipStream_t s) {
   switch (nch) {
-    case 1: return down_rn<R, 1>(p, max_tiles, s);
-    case 2: return down_rn<R, 2>(p, max_tiles, s);
-    case 3: return down_rn<R, 3>(p, max_tiles, s);
-    case 4: return down_rn<R, 4>(p, max_tiles, s);
+    case 1: return down_rn<R, 1>(p, max_union, s);
+    case 2: return down_rn<R, 2>(p, max_union, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_router(const uint16_t* x, const float* router_w, const float* gate_vec, double* partials,
-                         int rows, int h, int E, hipStream_t s) {
+hipError_t launch_router(const uint16_t* x, const float* router_w, const float* gate_vec, float* logits,
+                         float* gamma, int rows, int h, int E, hipStream_t s) {
   switch (rows) {
-    case 1: return router_r<1>(x, router_w, gate_vec, partials, h, E, s);
-    case 2: return router_r<2>(x, router_w, gate_vec, partials, h, E, s);
-    case 3: return router_r<3>(x, router_w, gate_vec, partials, h, E, s);
-    case 4: return router_r<4>(x, router_w, gate_vec, partials, h, E, s);
-    case 5: return router_r<5>(x, router_w, gate_vec, partials, h, E, s);
-    case 6: return router_r<6>(x, router_w, gate_vec, partials, h, E, s);
-    case 7: return router_r<7>(x, router_w, gate_vec, partials, h, E, s);
-    case 8: return router_r<8>(x, router_w, gate_vec, partials, h, E, s);
+    case 1: return router_r<1>(x, router_w, gate_vec, logits, gamma, h, E, s);
+    case 2: return router_r<2>(x, router_w, gate_vec, logits, gamma, h, E, s);
+    case 3: return router_r<3>(x, router_w, gate_vec, logits, gamma, h, E, s);
+    case 4: return router_r<4>(x, router_w, gate_vec, logits, gamma, h, E, s);
+    case 5: return router_r<5>(x, router_w, gate_vec, logits, gamma, h, E, s);
+    case 6: return router_r<6>(x, router_w, gate_vec, logits, gamma, h, E, s);
+    case 7: return router_r<7>(x, router_w, gate_vec, logits, gamma, h, E, s);
+    case 8: return router_r<8>(x, router_w, gate_vec, logits, gamma, h, E, s);
   }
   return hipErrorInvalidValue;
 }
@@ -613,9 +803,7 @@ hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids,
 
 hipError_t launch_gateup(const SweepParams& p, int rows, int max_union, hipStream_t s) {
   const int nch = (p.h + kChunk - 1) / kChunk;
-  const int tpe_r = (p.inter + kGateUpTile - 1) / kGateUpTile;
-  const int tpe_s = (p.shared_inter + kGateUpTile - 1) / kGateUpTile;
-  const int max_tiles = max_union * tpe_r + tpe_s;
+  const int max_tiles = max_union * p.inter + p.shared_inter;  // work items (rows)
   switch (rows) {
     case 1: return gateup_r<1>(p, nch, max_tiles, s);
     case 2: return gateup_r<2>(p, nch, max_tiles, s);
@@ -632,8 +820,7 @@ hipError_t launch_gateup(const SweepParams& p, int rows, int max_union, hipStrea
 hipError_t launch_down(const SweepParams& p, int rows, int max_union, hipStream_t s) {
   const int kmax = p.inter > p.shared_inter ? p.inter : p.shared_inter;
   const int nch = (kmax + kChunk - 1) / kChunk;
-  const int tpe = (p.h + kDownTile - 1) / kDownTile;
-  const int max_tiles = (max_union + 1) * tpe;
+  const int max_tiles = max_union;  // down_rn derives its tile count from the union bound
   switch (rows) {
     case 1: return down_r<1>(p, nch, max_tiles, s);
     case 2: return down_r<2>(p, nch, max_tiles, s);

@@ -83,7 +83,7 @@ def test_workspace_layout_is_ordered_and_aligned():
 
 
 @pytest.mark.parametrize("field,value", [
-    ("hidden", 0), ("hidden", 100), ("hidden", 16384), ("moe_inter", 48), ("shared_inter", 0),
+    ("hidden", 0), ("hidden", 100), ("hidden", 16384), ("moe_inter", 48), ("moe_inter", 8192), ("shared_inter", 0),
     ("num_experts", 0), ("num_experts", 2048), ("top_k", 0), ("top_k", 257), ("route_kind", 7),
     ("norm_topk_prob", 2), ("routed_scaling_factor", float("nan")),
 ])
