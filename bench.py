@@ -67,17 +67,16 @@ def step_bytes(shape, rows: int, U: int) -> dict:
     """Algorithmic HBM bytes of one step, split by stage."""
     h, E, k, I, Is = shape.hidden, shape.num_experts, shape.top_k, shape.moe_inter, shape.shared_inter
     pairs = rows * k
-    nkc = (h + 2047) // 2048
-    router = 4 * E * h + 4 * h + 2 * rows * h + 8 * nkc * rows * (E + 1)
-    topk = 8 * nkc * rows * (E + 1) + (4 * E if shape.route_kind == 1 else 0) + 8 * pairs
+    # route: router rows + gate vector + x, logits written and read back, bias, ids + weights out
+    route = (4 * E * h + 4 * h + 2 * rows * h + 8 * rows * (E + 1) + (4 * E if shape.route_kind == 1 else 0)
+             + 8 * pairs)
     gateup = 2 * U * expert_bytes(I, h) + 2 * expert_bytes(Is, h) + 2 * rows * h + 2 * (pairs * I + rows * Is)
     down = U * expert_bytes(h, I) + expert_bytes(h, Is) + 2 * (pairs * I + rows * Is) + 4 * (pairs + rows) * h
     blend = 4 * (pairs + rows) * h + 2 * rows * h + 8 * pairs
     # whole layer: weights + router + bias + gate vector + x in + out
     layer = (U * 3 * expert_bytes(I, h) + 3 * expert_bytes(Is, h) + 4 * E * h
              + (4 * E if shape.route_kind == 1 else 0) + 4 * h + 4 * rows * h)
-    return dict(layer=layer, router_gemv=router, topk_union=topk, gate_up_sweep=gateup, down_sweep=down,
-                blend=blend)
+    return dict(layer=layer, route=route, gate_up_sweep=gateup, down_sweep=down, blend=blend)
 
 
 def build_layers(shape, n_layers: int):

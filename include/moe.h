@@ -133,8 +133,16 @@ typedef struct moe_weights {
 
 /* Byte offsets of the intermediates moe_forward leaves in the workspace.
  * The layout depends on the config only (sized for MOE_MAX_ROWS rows).
- * Offsets are multiples of 256. */
+ * Offsets are multiples of 256.
+ *
+ * The workspace must be zero-filled (at least its first 256 bytes, the sync
+ * word) before its first use: the routing kernel counts its finished blocks
+ * there and the last one to finish runs top-k and the union.  Every call
+ * that returns MOE_OK leaves the word at zero again, so a workspace is
+ * zeroed once, not per call.  Calls sharing one workspace must not overlap
+ * in time (same stream, or ordered by events). */
 typedef struct moe_ws_layout {
+  size_t sync;          /* uint32 [1]                 arrival counter, zero between calls */
   size_t logits;        /* float  [MOE_MAX_ROWS][E]   router logits (row stride E)    */
   size_t gamma;         /* float  [MOE_MAX_ROWS]      sigmoid(x_r . shared gate)      */
   size_t topk_ids;      /* int32  [MOE_MAX_ROWS][k]   (row stride k)                  */
@@ -150,7 +158,8 @@ typedef struct moe_ws_layout {
   size_t total;         /* bytes needed                                               */
 } moe_ws_layout;
 
-/* Workspace bytes for ``cfg`` (any rows up to MOE_MAX_ROWS); 0 if cfg is invalid. */
+/* Workspace bytes for ``cfg`` (any rows up to MOE_MAX_ROWS); 0 if cfg is
+ * invalid.  Zero-fill the workspace once before its first use. */
 size_t moe_workspace_bytes(const moe_config* cfg);
 
 /* Fill ``out`` with the workspace layout of ``cfg``. */

@@ -42,8 +42,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-const char* const kStageNames[] = {"router_gemv", "topk_union", "gate_up_sweep", "down_sweep", "blend"};
-constexpr int kNumStages = 5;
+const char* const kStageNames[] = {"route", "gate_up_sweep", "down_sweep", "blend"};
+constexpr int kNumStages = 4;
 
 moe_status check_config(const moe_config* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
@@ -133,6 +133,7 @@ void compute_layout(const moe_config* c, moe_ws_layout* L) {
     off = round_up(off + bytes, 256);
     return o;
   };
+  L->sync = take(sizeof(uint32_t));
   L->logits = take(R * E * sizeof(float));
   L->gamma = take(R * sizeof(float));
   L->topk_ids = take(R * k * sizeof(int32_t));
@@ -174,19 +175,27 @@ moe_status device_status(hipError_t e, const char* what) {
   return MOE_OK;
 }
 
-void fill_topk(moe::TopkParams& p, const moe_config* c, const moe_weights* w, int32_t rows, char* ws,
-               const moe_ws_layout& L, int32_t* ids_out, float* w_out) {
+void fill_route(moe::RouteParams& p, const moe_config* c, const moe_weights* w, const uint16_t* x, int32_t rows,
+                char* ws, const moe_ws_layout& L, int32_t* ids_out, float* w_out) {
   memset(&p, 0, sizeof p);
-  p.bias = w->correction_bias;
+  p.x = x;
+  p.router_w = w->router_w;
+  p.gate_vec = w->shared_expert_gate;
+  p.h = c->hidden;
+  // Top-k reads bias[e] unconditionally; softmax routing ignores the value,
+  // so it reads the router weights (at least E floats) there instead.
+  p.bias = w->correction_bias ? w->correction_bias : w->router_w;
   p.E = c->num_experts;
   p.k = c->top_k;
   p.rows = rows;
   p.route_kind = c->route_kind;
   p.norm = c->norm_topk_prob;
   p.rsf = c->routed_scaling_factor;
-  p.logits = reinterpret_cast<const float*>(ws + L.logits);
+  p.logits = reinterpret_cast<float*>(ws + L.logits);
+  p.gamma = reinterpret_cast<float*>(ws + L.gamma);
   p.ids_out = ids_out;
   p.w_out = w_out;
+  p.counter = reinterpret_cast<uint32_t*>(ws + L.sync);
   p.union_ids = reinterpret_cast<int32_t*>(ws + L.union_ids);
   p.union_count = reinterpret_cast<int32_t*>(ws + L.union_count);
   p.slot_to_union = reinterpret_cast<int32_t*>(ws + L.slot_to_union);
@@ -221,10 +230,10 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
   };
   const int max_union = cfg->top_k * rows < cfg->num_experts ? cfg->top_k * rows : cfg->num_experts;
 
-  moe::TopkParams tp;
+  moe::RouteParams rp;
   int32_t* ids = reinterpret_cast<int32_t*>(wsb + L.topk_ids);
   float* wts = reinterpret_cast<float*>(wsb + L.topk_w);
-  fill_topk(tp, cfg, w, rows, wsb, L, ids, wts);
+  fill_route(rp, cfg, w, x, rows, wsb, L, ids, wts);
 
   moe::SweepParams sp;
   sp.x = x;
@@ -239,20 +248,16 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
 
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return device_status(e, "event record");
-  e = moe::launch_router(x, w->router_w, w->shared_expert_gate, reinterpret_cast<float*>(wsb + L.logits),
-                         reinterpret_cast<float*>(wsb + L.gamma), rows, cfg->hidden, cfg->num_experts, s);
-  if (e != hipSuccess) return device_status(e, "router launch");
+  if ((e = moe::launch_route(rp, true, s)) != hipSuccess) return device_status(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return device_status(e, "event record");
-  if ((e = moe::launch_topk(tp, true, s)) != hipSuccess) return device_status(e, "top-k launch");
-  if ((e = mark(2)) != hipSuccess) return device_status(e, "event record");
   if ((e = moe::launch_gateup(sp, rows, max_union, s)) != hipSuccess) return device_status(e, "gate/up launch");
-  if ((e = mark(3)) != hipSuccess) return device_status(e, "event record");
+  if ((e = mark(2)) != hipSuccess) return device_status(e, "event record");
   if ((e = moe::launch_down(sp, rows, max_union, s)) != hipSuccess) return device_status(e, "down launch");
-  if ((e = mark(4)) != hipSuccess) return device_status(e, "event record");
-  e = moe::launch_blend(sp.y, wts, tp.slot_to_union, reinterpret_cast<const float*>(wsb + L.gamma), out, rows,
+  if ((e = mark(3)) != hipSuccess) return device_status(e, "event record");
+  e = moe::launch_blend(sp.y, wts, rp.slot_to_union, reinterpret_cast<const float*>(wsb + L.gamma), out, rows,
                         cfg->hidden, cfg->top_k, s);
   if (e != hipSuccess) return device_status(e, "blend launch");
-  if ((e = mark(5)) != hipSuccess) return device_status(e, "event record");
+  if ((e = mark(4)) != hipSuccess) return device_status(e, "event record");
   return ok();
 }
 
@@ -292,13 +297,10 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t
   if (overlaps(topk_ids, nb, wsb, L.topk_ids) || overlaps(topk_w, nb, wsb, L.topk_ids))
     return fail(MOE_ERR_INVALID_ARG, "topk outputs overlap the router intermediates of the workspace");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  moe::TopkParams tp;
-  fill_topk(tp, cfg, w, rows, wsb, L, topk_ids, topk_w);
-  hipError_t e = moe::launch_router(x_bf16, w->router_w, w->shared_expert_gate,
-                                    reinterpret_cast<float*>(wsb + L.logits), reinterpret_cast<float*>(wsb + L.gamma),
-                                    rows, cfg->hidden, cfg->num_experts, s);
-  if (e != hipSuccess) return device_status(e, "router launch");
-  if ((e = moe::launch_topk(tp, false, s)) != hipSuccess) return device_status(e, "top-k launch");
+  moe::RouteParams rp;
+  fill_route(rp, cfg, w, x_bf16, rows, wsb, L, topk_ids, topk_w);
+  hipError_t e = moe::launch_route(rp, false, s);
+  if (e != hipSuccess) return device_status(e, "route launch");
   return ok();
 }
 

@@ -123,25 +123,17 @@ __device__ __forceinline__ double wave_sum(double v) {
   return __builtin_bit_cast(double, (hi << 32) | lo);
 }
 
-// Maximum over the 64 lanes (same DPP pattern as wave_sum), returned to every lane.
-__device__ __forceinline__ uint64_t wave_max(uint64_t v) {
-  auto step = [](uint64_t a, uint64_t o) { return o > a ? o : a; };
-#define MOE_DPP_MAX_STEP(CTRL, MASK)                                                   \
-  {                                                                                    \
-    const uint64_t lo = dpp_u32<CTRL, MASK>((uint32_t)v);                              \
-    const uint64_t hi = dpp_u32<CTRL, MASK>((uint32_t)(v >> 32));                      \
-    v = step(v, (hi << 32) | lo);                                                      \
-  }
-  MOE_DPP_MAX_STEP(0xB1, 0xF)
-  MOE_DPP_MAX_STEP(0x4E, 0xF)
-  MOE_DPP_MAX_STEP(0x141, 0xF)
-  MOE_DPP_MAX_STEP(0x140, 0xF)
-  MOE_DPP_MAX_STEP(0x142, 0xA)
-  MOE_DPP_MAX_STEP(0x143, 0xC)
-#undef MOE_DPP_MAX_STEP
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return (hi << 32) | lo;
+// Maximum over the 64 lanes (same DPP pattern as wave_sum; lanes a step
+// does not reach read 0, the identity), returned to every lane.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u32<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+  v = mx(v, dpp_u32<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+  v = mx(v, dpp_u32<0x141, 0xF>(v));  // row_half_mirror
+  v = mx(v, dpp_u32<0x140, 0xF>(v));  // row_mirror
+  v = mx(v, dpp_u32<0x142, 0xA>(v));  // row_bcast:15
+  v = mx(v, dpp_u32<0x143, 0xC>(v));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // The wave's index within its block, as a scalar (wave-uniform) value.

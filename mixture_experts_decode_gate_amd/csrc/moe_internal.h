@@ -10,13 +10,19 @@ namespace moe {
 
 struct SlotInfo;
 
-struct TopkParams {
-  const float* bias;       // [E] or null (softmax)
+struct RouteParams {
+  const uint16_t* x;       // [rows][h] bf16
+  const float* router_w;   // [E][h]
+  const float* gate_vec;   // [h] shared-expert gate vector
+  int h;
+  const float* bias;       // [E]; for softmax any readable [E] floats (ignored)
   int E, k, rows, route_kind, norm;
   float rsf;
-  const float* logits;     // [8][E], written by the router kernel
+  float* logits;           // [8][E]
+  float* gamma;            // [8]
   int32_t* ids_out;        // [rows][k]
   float* w_out;            // [rows][k]
+  uint32_t* counter;       // arrival counter: zero between calls
   // union outputs (moe_forward only)
   int32_t* union_ids;
   int32_t* union_count;
@@ -42,9 +48,7 @@ struct SweepParams {
 
 constexpr size_t kSlotInfoBytes = 72;  // sizeof(SlotInfo), checked in the kernels file
 
-hipError_t launch_router(const uint16_t* x, const float* router_w, const float* gate_vec, float* logits,
-                         float* gamma, int rows, int h, int E, hipStream_t s);
-hipError_t launch_topk(const TopkParams& p, bool with_union, hipStream_t s);
+hipError_t launch_route(const RouteParams& p, bool with_union, hipStream_t s);
 hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids, int32_t* union_count,
                         int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);
 hipError_t launch_gateup(const SweepParams& p, int rows, int max_union, hipStream_t s);

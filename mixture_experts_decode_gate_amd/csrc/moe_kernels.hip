@@ -23,89 +23,47 @@
 
 namespace moe {
 
-// ---------------------------------------------------------------- router
-// One block per router row e (e == E is the shared expert's gate vector), one
-// wave per kRouterChunk-column chunk.  Every load of a wave is issued before
-// any arithmetic; each lane accumulates its columns in fp64, the wave reduces
-// in a fixed order, and the chunk partials are summed in chunk order and
-// rounded once: logits[r][e] = fp32(sum), gamma[r] = fp32(sigmoid(sum)).
+// ---------------------------------------------------------------- routing
+// One kernel: router GEMV, top-k, union and slot resolution.
+//
+// Block e (of E+1) computes router row e for every input row (e == E is the
+// shared expert's gate vector): wave c < nkc takes the kRouterChunk-column
+// chunk c, issues all its loads before any arithmetic, accumulates in fp64
+// and reduces in a fixed order; the chunk partials are summed in chunk order
+// and rounded once: logits[r][e] = fp32(sum), gamma[r] = fp32(sigmoid(sum)).
+// Each block then publishes its results (device-scope fence) and takes a
+// ticket from the arrival counter; the block that draws the last ticket reads
+// every logit and runs top-k (one wave per row), the union (wave 0) and the
+// slot resolution, then resets the counter to zero for the next call.
 constexpr int kRouterChunk = 1024;
 constexpr int kMaxRouterChunks = MOE_MAX_DIM / kRouterChunk;
+constexpr int kRouteThreads = 64 * kMaxRows;  // >= one wave per row for top-k, >= nkc waves
+static_assert(kMaxRouterChunks <= kMaxRows, "route blocks need a wave per router chunk");
+static_assert(MOE_MAX_EXPERTS <= 64 * 16, "top-k holds at most 16 keys per lane");
 
-template <int R>
-__global__ __launch_bounds__(64 * kMaxRouterChunks) void router_kernel(const uint16_t* __restrict__ x,
-                                                                       const float* __restrict__ router_w,
-                                                                       const float* __restrict__ gate_vec,
-                                                                       float* __restrict__ logits,
-                                                                       float* __restrict__ gamma, int h, int E) {
-  __shared__ double part[kMaxRouterChunks][kMaxRows];
-  const int lane = threadIdx.x & 63;
-  const int c = wave_id();
-  const int nkc = blockDim.x >> 6;
-  const int e = blockIdx.x;
-  const float* row = (e < E) ? router_w + (size_t)e * h : gate_vec;
-  constexpr int kIt = kRouterChunk / 256;
-  float4 wv[kIt];
-  uint2 xv[R][kIt];
-  bool ok[kIt];
-#pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    const int col = c * kRouterChunk + it * 256 + lane * 4;
-    ok[it] = col < h;
-    const int cc = ok[it] ? col : h - 4;  // in-bounds; the contribution is dropped below
-    const u32x4 w4 = ld_stream(reinterpret_cast<const uint8_t*>(row + cc));
-    wv[it] = make_float4(__uint_as_float(w4.x), __uint_as_float(w4.y), __uint_as_float(w4.z), __uint_as_float(w4.w));
-#pragma unroll
-    for (int r = 0; r < R; ++r) xv[r][it] = *reinterpret_cast<const uint2*>(x + (size_t)r * h + cc);
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    double acc = 0.0;
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const double w0 = ok[it] ? (double)wv[it].x : 0.0, w1 = ok[it] ? (double)wv[it].y : 0.0;
-      const double w2 = ok[it] ? (double)wv[it].z : 0.0, w3 = ok[it] ? (double)wv[it].w : 0.0;
-      acc = __builtin_fma((double)bf16_to_f32(xv[r][it].x & 0xFFFFu), w0, acc);
-      acc = __builtin_fma((double)bf16_to_f32(xv[r][it].x >> 16), w1, acc);
-      acc = __builtin_fma((double)bf16_to_f32(xv[r][it].y & 0xFFFFu), w2, acc);
-      acc = __builtin_fma((double)bf16_to_f32(xv[r][it].y >> 16), w3, acc);
-    }
-    const double s = wave_sum(acc);
-    if (lane == 0) part[c][r] = s;
-  }
-  __syncthreads();
-  if (threadIdx.x < R) {
-    const int r = threadIdx.x;
-    double z = 0.0;
-    for (int cc = 0; cc < nkc; ++cc) z += part[cc][r];
-    if (e < E)
-      logits[r * E + e] = (float)z;
-    else
-      gamma[r] = (float)(1.0 / (1.0 + exp(-z)));
-  }
-}
-
-// ---------------------------------------------------------------- union
-// One wave deduplicates n <= 64 ids held in LDS: lane t compares its id with
-// every slot (pairwise scan, no sort).  A slot is a first occurrence when no
-// earlier slot holds its id; first occurrences, in slot order, form the union.
-__device__ void union_wave(const int32_t* ids_lds, int n, int k, int lane, int32_t* union_ids,
-                           int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask,
-                           int32_t* first_out, uint32_t* mask_out) {
+// Union of the n <= 64 ids in ids_lds (slot t = r*k + j).  Lane t compares its
+// id with every slot at once (broadcast LDS reads, no sort): slot t is a first
+// occurrence when no earlier slot holds its id.  First occurrences, in slot
+// order, form the union.  Returns the lane's union position if it is a first
+// occurrence (else -1) and, in *mask_out, the rows that chose its id.
+__device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows, int lane, int32_t* union_ids,
+                          int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask, uint32_t* mask_out) {
   const int id = lane < n ? ids_lds[lane] : -1;
-  int first = lane;
-  uint32_t mask = 0;
-  int row = 0, col = 0;
-  for (int t = 0; t < n; ++t) {
-    const int v = __builtin_amdgcn_readlane(id, t);  // slot t's id, broadcast
-    const bool eq = (lane < n) && (v == id);
-    if (eq && t < first) first = t;
-    if (eq) mask |= 1u << row;
-    if (++col == k) {
-      col = 0;
-      ++row;
-    }
+  uint64_t eq = 0;
+#pragma unroll
+  for (int t4 = 0; t4 < kMaxIds / 4; ++t4) {
+    const int4 v = reinterpret_cast<const int4*>(ids_lds)[t4];
+    eq |= (uint64_t)(v.x == id) << (4 * t4 + 0);
+    eq |= (uint64_t)(v.y == id) << (4 * t4 + 1);
+    eq |= (uint64_t)(v.z == id) << (4 * t4 + 2);
+    eq |= (uint64_t)(v.w == id) << (4 * t4 + 3);
   }
+  eq &= n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+  const int first = lane < n ? __builtin_ctzll(eq) : lane;
+  uint32_t mask = 0;
+  const uint64_t kmask = k >= 64 ? ~0ull : ((1ull << k) - 1ull);
+  for (int r = 0; r < rows; ++r)
+    if ((eq >> (r * k)) & kmask) mask |= 1u << r;
   const bool is_first = (lane < n) && (first == lane);
   const unsigned long long bal = __ballot(is_first);
   const int pos_self = __popcll(bal & ((1ull << lane) - 1ull));
@@ -116,151 +74,215 @@ __device__ void union_wave(const int32_t* ids_lds, int n, int k, int lane, int32
     if (row_mask) row_mask[pos_self] = mask;
   }
   if (lane == 0) *union_count = __popcll(bal);
-  *first_out = is_first ? pos_self : -1;
   *mask_out = mask;
+  return is_first ? pos_self : -1;
 }
 
-__global__ __launch_bounds__(64) void union_kernel(const int32_t* __restrict__ ids, int n, int k,
+__global__ __launch_bounds__(64) void union_kernel(const int32_t* __restrict__ ids, int rows, int k,
                                                    int32_t* union_ids, int32_t* union_count,
                                                    int32_t* slot_to_union, uint32_t* row_mask) {
-  __shared__ int32_t s_ids[kMaxIds];
+  __shared__ __align__(16) int32_t s_ids[kMaxIds];
   const int lane = threadIdx.x;
-  if (lane < n) s_ids[lane] = ids[lane];
+  const int n = rows * k;
+  s_ids[lane] = lane < n ? ids[lane] : -1;
   __syncthreads();
-  int pos;
   uint32_t mask;
-  union_wave(s_ids, n, k, lane, union_ids, union_count, slot_to_union, row_mask, &pos, &mask);
+  union_wave(s_ids, n, k, rows, lane, union_ids, union_count, slot_to_union, row_mask, &mask);
 }
 
-// ---------------------------------------------------------------- top-k
-// One wave per row: logits (fp32 rounding of the fp64 sum over chunks),
-// selection keys, k rounds of wave argmax (ties to the lower id), weights in
-// fp64.  With UNION, wave 0 then builds the union and resolves each union
-// slot's weight pointers for the sweeps.
-constexpr int kKeysPerLane = MOE_MAX_EXPERTS / 64;
+// Order-preserving map of a float key to uint32 (larger float -> larger
+// integer); +0 and -0 map to neighbours, never to 0 except the all-ones NaN.
+__device__ __forceinline__ uint32_t key_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
 
-template <bool UNION>
-__global__ __launch_bounds__(512) void topk_kernel(TopkParams p) {
-  __shared__ int32_t s_ids[kMaxIds];
-  const int lane = threadIdx.x & 63;
-  const int r = threadIdx.x >> 6;
+// Top-k of row r (one wave).  Lane l holds experts l*G .. l*G+G-1, so a lower
+// (lane, position) pair is a lower expert id.  Each of the k rounds takes the
+// lane's largest remaining key (lowest position on ties), the wave-wide
+// maximum of those, and the lowest lane holding it: the largest key, ties to
+// the lower id.  Weights follow in fp64.  Writes ids and weights of the row
+// to ids_out/w_out and the ids to s_ids.
+template <int G>
+__device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids) {
   const int E = p.E, k = p.k;
-  if (r < p.rows) {
-    float kv[kKeysPerLane];
-    float lv[kKeysPerLane];
-    int selj[kKeysPerLane];
+  float lv[G], bv[G];
+  // Every load first (clamped in-bounds indices, no branch) so they overlap.
 #pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) {
-      const int e = lane + 64 * i;
-      kv[i] = -__builtin_huge_valf();
-      lv[i] = 0.f;
-      selj[i] = -1;
-      if (i * 64 < E && e < E) {
-        const float L32 = p.logits[r * E + e];
-        lv[i] = L32;
-        if (p.route_kind == MOE_ROUTE_SOFTMAX) {
-          kv[i] = L32;
-        } else {
-          const float s32 = (float)(1.0 / (1.0 + exp(-(double)L32)));
-          kv[i] = s32 + p.bias[e];
-        }
-      }
+  for (int i = 0; i < G; ++i) {
+    const int e = min(lane * G + i, E - 1);
+    lv[i] = p.logits[r * E + e];
+    bv[i] = p.bias[e];
+  }
+  const bool softmax = p.route_kind == MOE_ROUTE_SOFTMAX;
+  uint32_t key[G];  // 0: not a candidate (past E, or already taken)
+  double sv[G];     // sigmoid score (sigmoid routing)
+  int selj[G];      // round that took the expert, -1 if none
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const bool valid = lane * G + i < E;
+    float kf = lv[i];
+    sv[i] = 0.0;
+    if (!softmax && valid) {
+      sv[i] = 1.0 / (1.0 + exp(-(double)lv[i]));
+      kf = (float)sv[i] + bv[i];
     }
-    // Selection: the key maps to an order-preserving uint32 and packs with
-    // ~e into a uint64, so the wave maximum is the largest key, ties to the
-    // lower id.  Invalid or taken entries are 0.
-    float top_logit = 0.f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = 0;
+    key[i] = valid ? key_bits(kf) : 0u;
+    selj[i] = -1;
+  }
+  float top_logit = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t best = 0;
+    int bi = 0;
 #pragma unroll
-      for (int i = 0; i < kKeysPerLane; ++i) {
-        const int e = lane + 64 * i;
-        if (i * 64 < E && e < E && selj[i] < 0) {
-          uint32_t u = __float_as_uint(kv[i]);
-          u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-          const uint64_t pk = ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-          best = pk > best ? pk : best;
-        }
-      }
-      best = wave_max(best);
-      int be = (int)(0xFFFFFFFFu - (uint32_t)best);
-      // NaN keys (outside the contract) can leave no winner; keep the id in
-      // range so no later stage indexes the weight tables out of bounds.
-      if (best == 0 || be >= E || be < 0) be = 0;
-      if ((be & 63) == lane) {
-#pragma unroll
-        for (int i = 0; i < kKeysPerLane; ++i)
-          if (i == (be >> 6)) selj[i] = j;
-      }
-      if (lane == 0) {
-        p.ids_out[r * k + j] = be;
-        s_ids[r * k + j] = be;
-      }
-      if (j == 0) {
-        // softmax: the largest logit is the first winner's logit (key == logit)
-        uint32_t u = (uint32_t)(best >> 32);
-        u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-        top_logit = __uint_as_float(u);
-      }
+    for (int i = 0; i < G; ++i) {
+      const bool better = key[i] > best;
+      best = better ? key[i] : best;
+      bi = better ? i : bi;
     }
-    // Weights.  Softmax: exp(L - max) normalised over all experts, or over the
-    // k selected when norm_topk_prob.  Sigmoid: s, optionally normalised over
-    // the selected, times routed_scaling_factor.
-    double num[kKeysPerLane];
-    double all_part = 0.0, sel_part = 0.0;
+    const uint32_t m = wave_max(best);
+    const uint64_t cand = __ballot(best == m);
+    const int wl = (int)__builtin_ctzll(cand | (1ull << 63));
+    const int wi = __builtin_amdgcn_readlane(bi, wl);
+    // k <= E valid keys keep m > 0; the clamp only guards ids against keys
+    // outside the contract (NaN).
+    const int be = min(wl * G + wi, E - 1);
+    if (lane == wl) {
 #pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) {
-      const int e = lane + 64 * i;
-      num[i] = 0.0;
-      if (e < E) {
-        double v;
-        if (p.route_kind == MOE_ROUTE_SOFTMAX)
-          v = exp((double)lv[i] - (double)top_logit);
-        else
-          v = 1.0 / (1.0 + exp(-(double)lv[i]));
-        num[i] = v;
-        all_part += v;
-        if (selj[i] >= 0) sel_part += v;
-      }
-    }
-    const double all_sum = wave_sum(all_part);
-    const double sel_sum = wave_sum(sel_part);
-#pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) {
-      if (selj[i] >= 0) {
-        double wgt;
-        if (p.route_kind == MOE_ROUTE_SOFTMAX) {
-          wgt = p.norm ? num[i] / sel_sum : num[i] / all_sum;
-        } else {
-          wgt = p.norm ? num[i] / sel_sum : num[i];
-          wgt *= (double)p.rsf;
+      for (int i = 0; i < G; ++i)
+        if (i == wi) {
+          key[i] = 0u;
+          selj[i] = j;
         }
-        p.w_out[r * k + selj[i]] = (float)wgt;
-      }
+    }
+    if (j == 0) top_logit = key_float(m);  // softmax: the largest logit
+    if (lane == 0) {
+      p.ids_out[r * k + j] = be;
+      s_ids[r * k + j] = be;
     }
   }
-  if constexpr (UNION) {
+  // Weights.  Softmax: exp(L - max), normalised over all experts, or over the
+  // k selected when norm_topk_prob.  Sigmoid: s, optionally normalised over
+  // the selected, times routed_scaling_factor.
+  double all_part = 0.0, sel_part = 0.0;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    if (lane * G + i < E) {
+      if (softmax && (!p.norm || selj[i] >= 0)) sv[i] = exp((double)lv[i] - (double)top_logit);
+      all_part += sv[i];
+      if (selj[i] >= 0) sel_part += sv[i];
+    }
+  }
+  const double all_sum = softmax && !p.norm ? wave_sum(all_part) : 1.0;
+  const double sel_sum = p.norm ? wave_sum(sel_part) : 1.0;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    if (selj[i] >= 0) {
+      double wgt;
+      if (softmax) {
+        wgt = p.norm ? sv[i] / sel_sum : sv[i] / all_sum;
+      } else {
+        wgt = p.norm ? sv[i] / sel_sum : sv[i];
+        wgt *= (double)p.rsf;
+      }
+      p.w_out[r * k + selj[i]] = (float)wgt;
+    }
+  }
+}
+
+template <int R, int G>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int with_union) {
+  __shared__ double part[kMaxRouterChunks][kMaxRows];
+  __shared__ __align__(16) int32_t s_ids[kMaxIds];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int h = p.h, E = p.E;
+  const int nkc = (h + kRouterChunk - 1) / kRouterChunk;
+  const int e = blockIdx.x;
+
+  if (wave < nkc) {
+    const int c = wave;
+    const float* row = (e < E) ? p.router_w + (size_t)e * h : p.gate_vec;
+    constexpr int kIt = kRouterChunk / 256;
+    float4 wv[kIt];
+    uint2 xv[R][kIt];
+    bool ok[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int col = c * kRouterChunk + it * 256 + lane * 4;
+      ok[it] = col < h;
+      const int cc = ok[it] ? col : h - 4;  // in-bounds; the contribution is dropped below
+      const u32x4 w4 = ld_stream(reinterpret_cast<const uint8_t*>(row + cc));
+      wv[it] = make_float4(__uint_as_float(w4.x), __uint_as_float(w4.y), __uint_as_float(w4.z), __uint_as_float(w4.w));
+#pragma unroll
+      for (int r = 0; r < R; ++r) xv[r][it] = *reinterpret_cast<const uint2*>(p.x + (size_t)r * h + cc);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      double acc = 0.0;
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const double w0 = ok[it] ? (double)wv[it].x : 0.0, w1 = ok[it] ? (double)wv[it].y : 0.0;
+        const double w2 = ok[it] ? (double)wv[it].z : 0.0, w3 = ok[it] ? (double)wv[it].w : 0.0;
+        acc = __builtin_fma((double)bf16_to_f32(xv[r][it].x & 0xFFFFu), w0, acc);
+        acc = __builtin_fma((double)bf16_to_f32(xv[r][it].x >> 16), w1, acc);
+        acc = __builtin_fma((double)bf16_to_f32(xv[r][it].y & 0xFFFFu), w2, acc);
+        acc = __builtin_fma((double)bf16_to_f32(xv[r][it].y >> 16), w3, acc);
+      }
+      const double s = wave_sum(acc);
+      if (lane == 0) part[c][r] = s;
+    }
+  }
+  __syncthreads();
+  // Thread 0 writes the block's results and takes a ticket with release
+  // order (its own stores become visible before the increment).  The block
+  // drawing the last ticket acquires, so its reads see every block's results.
+  // A full fence in every block would also invalidate every L2 on each
+  // arrival, which costs far more than the whole GEMV.
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      double z = 0.0;
+      for (int cc = 0; cc < nkc; ++cc) z += part[cc][r];
+      if (e < E)
+        p.logits[r * E + e] = (float)z;
+      else
+        p.gamma[r] = (float)(1.0 / (1.0 + exp(-z)));
+    }
+    const uint32_t ticket = __hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = ticket == gridDim.x - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  if (wave < R) topk_row<G>(p, wave, lane, s_ids);
+  if (with_union) {
     __syncthreads();
-    if (threadIdx.x < 64) {
-      int pos;
+    if (wave == 0) {
       uint32_t mask;
-      union_wave(s_ids, p.rows * k, k, lane, p.union_ids, p.union_count, p.slot_to_union, p.row_mask,
-                 &pos, &mask);
+      const int pos = union_wave(s_ids, R * p.k, p.k, R, lane, p.union_ids, p.union_count, p.slot_to_union,
+                                 p.row_mask, &mask);
       if (pos >= 0) {
-        const int e = s_ids[lane];
+        const int ex = s_ids[lane];
         SlotInfo si;
-        si.gate_packed = p.gate.packed[e];
-        si.gate_scales = p.gate.scales[e];
-        si.up_packed = p.up.packed[e];
-        si.up_scales = p.up.scales[e];
-        si.down_packed = p.down.packed[e];
-        si.down_scales = p.down.scales[e];
-        si.gate_scale2 = p.gate.scale2[e];
-        si.up_scale2 = p.up.scale2[e];
-        si.down_scale2 = p.down.scale2[e];
+        si.gate_packed = p.gate.packed[ex];
+        si.gate_scales = p.gate.scales[ex];
+        si.up_packed = p.up.packed[ex];
+        si.up_scales = p.up.scales[ex];
+        si.down_packed = p.down.packed[ex];
+        si.down_scales = p.down.scales[ex];
+        si.gate_scale2 = p.gate.scale2[ex];
+        si.up_scale2 = p.up.scale2[ex];
+        si.down_scale2 = p.down.scale2[ex];
         si.inter = p.inter;
         si.row_mask = mask;
-        si.expert = e;
+        si.expert = ex;
         p.slots[pos] = si;
       }
       if (lane == 0) {
@@ -275,12 +297,14 @@ __global__ __launch_bounds__(512) void topk_kernel(TopkParams p) {
         si.up_scale2 = p.shared_up.scale2;
         si.down_scale2 = p.shared_down.scale2;
         si.inter = p.shared_inter;
-        si.row_mask = (1u << p.rows) - 1u;
+        si.row_mask = (1u << R) - 1u;
         si.expert = -1;
         p.slots[kSharedSlot] = si;
       }
     }
   }
+  // every other block has arrived: reset for the next call
+  if (threadIdx.x == 0) __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- sweeps
@@ -439,23 +463,40 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   };
 
   if (cur.su > U) return;
-  // Loads of the next item are always issued (the current item again on the
-  // last step) so no branch separates them from the compute that overlaps them.
+  // Three register buffers in rotation: while one item is computed, the next
+  // two are in flight.  Loads are always issued (a repeat of the last item
+  // past the end) so no branch separates them from the compute they overlap.
+  RowRegs<NCH> gc, uc;
+  SlotInfo sc;
+  int nc = 0, slot_c = 0;
+  ItemCursor c1 = cur, c2 = cur;
+  advance(c1, W, U, p.inter, p.shared_inter);
+  bool more1 = c1.su <= U;
   fetch(cur, ga, ua, sa, na, slot_a);
+  fetch(more1 ? c1 : cur, gb, ub, sb, nb, slot_b);
   while (true) {
-    ItemCursor nxt = cur;
-    advance(nxt, W, U, p.inter, p.shared_inter);
-    const bool more = nxt.su <= U;
-    fetch(more ? nxt : cur, gb, ub, sb, nb, slot_b);
+    c2 = more1 ? c1 : cur;
+    advance(c2, W, U, p.inter, p.shared_inter);
+    bool more2 = more1 && c2.su <= U;
+    fetch(more2 ? c2 : cur, gc, uc, sc, nc, slot_c);
     compute(ga, ua, sa, na, slot_a);
-    if (!more) break;
-    cur = nxt;
-    advance(nxt, W, U, p.inter, p.shared_inter);
-    const bool more2 = nxt.su <= U;
-    fetch(more2 ? nxt : cur, ga, ua, sa, na, slot_a);
+    if (!more1) break;
+    // rotate: b -> a role
+    ItemCursor c3 = more2 ? c2 : cur;
+    advance(c3, W, U, p.inter, p.shared_inter);
+    bool more3 = more2 && c3.su <= U;
+    fetch(more3 ? c3 : cur, ga, ua, sa, na, slot_a);
     compute(gb, ub, sb, nb, slot_b);
     if (!more2) break;
-    cur = nxt;
+    ItemCursor c4 = more3 ? c3 : cur;
+    advance(c4, W, U, p.inter, p.shared_inter);
+    bool more4 = more3 && c4.su <= U;
+    fetch(more4 ? c4 : cur, gb, ub, sb, nb, slot_b);
+    compute(gc, uc, sc, nc, slot_c);
+    if (!more3) break;
+    cur = c3;
+    c1 = c4;
+    more1 = more4;
   }
 }
 
@@ -706,10 +747,12 @@ dim3 sweep_grid(K kernel, size_t lds, int max_blocks, SweepShape& cache, int def
 }
 
 template <int R>
-hipError_t router_r(const uint16_t* x, const float* rw, const float* gv, float* logits, float* gamma, int h, int E,
-                    hipStream_t s) {
-  const int nkc = (h + kRouterChunk - 1) / kRouterChunk;
-  hipLaunchKernelGGL((router_kernel<R>), dim3(E + 1), dim3(64 * nkc), 0, s, x, rw, gv, logits, gamma, h, E);
+hipError_t route_r(const RouteParams& p, bool with_union, hipStream_t s) {
+  // keys per lane: 4 covers up to 256 experts, 16 up to MOE_MAX_EXPERTS
+  if (p.E <= 256)
+    hipLaunchKernelGGL((route_kernel<R, 4>), dim3(p.E + 1), dim3(kRouteThreads), 0, s, p, (int)with_union);
+  else
+    hipLaunchKernelGGL((route_kernel<R, 16>), dim3(p.E + 1), dim3(kRouteThreads), 0, s, p, (int)with_union);
   return hipGetLastError();
 }
 
@@ -771,32 +814,27 @@ hipError_t down_r(const SweepParams& p, int nch, int max_union, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_router(const uint16_t* x, const float* router_w, const float* gate_vec, float* logits,
-                         float* gamma, int rows, int h, int E, hipStream_t s) {
-  switch (rows) {
-    case 1: return router_r<1>(x, router_w, gate_vec, logits, gamma, h, E, s);
-    case 2: return router_r<2>(x, router_w, gate_vec, logits, gamma, h, E, s);
-    case 3: return router_r<3>(x, router_w, gate_vec, logits, gamma, h, E, s);
-    case 4: return router_r<4>(x, router_w, gate_vec, logits, gamma, h, E, s);
-    case 5: return router_r<5>(x, router_w, gate_vec, logits, gamma, h, E, s);
-    case 6: return router_r<6>(x, router_w, gate_vec, logits, gamma, h, E, s);
-    case 7: return router_r<7>(x, router_w, gate_vec, logits, gamma, h, E, s);
-    case 8: return router_r<8>(x, router_w, gate_vec, logits, gamma, h, E, s);
+hipError_t launch_route(const RouteParams& p, bool with_union, hipStream_t s) {
+  switch (p.rows) {
+#define MOE_ROUTE_CASE(R) \
+  case R:                 \
+    return route_r<R>(p, with_union, s);
+    MOE_ROUTE_CASE(1)
+    MOE_ROUTE_CASE(2)
+    MOE_ROUTE_CASE(3)
+    MOE_ROUTE_CASE(4)
+    MOE_ROUTE_CASE(5)
+    MOE_ROUTE_CASE(6)
+    MOE_ROUTE_CASE(7)
+    MOE_ROUTE_CASE(8)
+#undef MOE_ROUTE_CASE
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_topk(const TopkParams& p, bool with_union, hipStream_t s) {
-  if (with_union)
-    hipLaunchKernelGGL((topk_kernel<true>), dim3(1), dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL((topk_kernel<false>), dim3(1), dim3(512), 0, s, p);
-  return hipGetLastError();
-}
-
 hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids, int32_t* union_count,
                         int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s) {
-  hipLaunchKernelGGL(union_kernel, dim3(1), dim3(64), 0, s, ids, rows * k, k, union_ids, union_count,
+  hipLaunchKernelGGL(union_kernel, dim3(1), dim3(64), 0, s, ids, rows, k, union_ids, union_count,
                      slot_to_union, row_mask);
   return hipGetLastError();
 }

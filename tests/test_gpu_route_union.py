@@ -39,25 +39,27 @@ class RouteWeights:
         w.shared_expert_gate = self.gate_vec.data_ptr()
         self.weights = w
 
-    def run(self, x_bits):
+    def run(self, x_bits, ws=None):
         torch = torch_cuda()
         moe = moe_mod()
         R, k = x_bits.shape[0], self.shape.top_k
         ids = torch.full((R, k), -1, dtype=torch.int32, device="cuda")
         wts = torch.zeros((R, k), dtype=torch.float32, device="cuda")
-        ws = ws_for(self.cfg)
+        ws = ws_for(self.cfg) if ws is None else ws
         moe.moe_route(self.cfg, self.weights, x_dev(x_bits), ids, wts, ws)
         torch.cuda.synchronize()
         L = moe.moe_workspace_layout(self.cfg)
+        # the routing kernel's arrival counter is back at zero after every call
+        assert ws_read(ws, L.sync, np.uint32, 1)[0] == 0
         E = self.shape.num_experts
         logits = ws_read(ws, L.logits, np.float32, 8 * E).reshape(8, E)[:R]
         gamma = ws_read(ws, L.gamma, np.float32, 8)[:R]
         return ids.cpu().numpy(), wts.cpu().numpy(), logits, gamma
 
 
-def check_route(rw, x_bits):
+def check_route(rw, x_bits, ws=None):
     s = rw.shape
-    ids, wts, logits, gamma = rw.run(x_bits)
+    ids, wts, logits, gamma = rw.run(x_bits, ws)
     L_ref, ids_ref, w_ref = RT.route(x_bits, rw.router_w_np, rw.bias_np, s.route_kind, s.top_k, s.norm_topk_prob,
                                      s.routed_scaling_factor)
     gamma_ref = RT.shared_gate(x_bits, rw.gate_vec_np)
@@ -84,6 +86,23 @@ def test_route_rows_256_experts(rows):
     shape = synth.CONFIGS["c4_e256_prefill8"]
     rw = RouteWeights(shape)
     check_route(rw, synth.activations(shape, 11, rows=rows))
+
+
+def test_route_largest_shape():
+    # MOE_MAX_DIM columns (8 router chunks, one per wave) and MOE_MAX_EXPERTS experts
+    shape = synth.MoeShape("max", 8192, 1024, 8, 64, 64, 8, synth.ROUTE_SIGMOID_BIAS, True, 2.5)
+    rw = RouteWeights(shape)
+    check_route(rw, synth.activations(shape, 3))
+
+
+def test_route_one_workspace_many_calls():
+    # Calls with different row counts share one workspace back to back: each
+    # one must find the arrival counter at zero and leave it there.
+    shape = synth.CONFIGS["c3_e256_verify4"]
+    rw = RouteWeights(shape)
+    ws = ws_for(rw.cfg)
+    for step, rows in enumerate([4, 1, 8, 2, 8, 1]):
+        check_route(rw, synth.activations(shape, 20 + step, rows=rows), ws)
 
 
 def test_route_exact_ties_pick_lower_id():
