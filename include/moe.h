@@ -135,15 +135,16 @@ typedef struct moe_weights {
  * The layout depends on the config only (sized for MOE_MAX_ROWS rows).
  * Offsets are multiples of 256.
  *
- * The workspace must be zero-filled (at least its first 256 bytes, the sync
- * word) before its first use: the routing kernel counts its finished blocks
- * there and the last one to finish runs top-k and the union.  Every call
- * that returns MOE_OK leaves the word at zero again, so a workspace is
- * zeroed once, not per call.  Calls sharing one workspace must not overlap
- * in time (same stream, or ordered by events). */
+ * The workspace must be zero-filled (its first 256 bytes suffice) before
+ * its first use: the routing kernel counts its finished blocks in the first
+ * word (the last block to finish runs top-k and the union) and resets that
+ * word before it ends, so a workspace is zeroed once, not per call.  Calls
+ * sharing one workspace must not overlap in time (same stream, or ordered
+ * by events). */
 typedef struct moe_ws_layout {
   size_t sync;          /* uint32 [1]                 arrival counter, zero between calls */
   size_t logits;        /* float  [MOE_MAX_ROWS][E]   router logits (row stride E)    */
+  size_t score;         /* double [MOE_MAX_ROWS][E]   sigmoid(logit) for sigmoid routing */
   size_t gamma;         /* float  [MOE_MAX_ROWS]      sigmoid(x_r . shared gate)      */
   size_t topk_ids;      /* int32  [MOE_MAX_ROWS][k]   (row stride k)                  */
   size_t topk_w;        /* float  [MOE_MAX_ROWS][k]                                   */

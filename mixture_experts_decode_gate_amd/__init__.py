@@ -70,7 +70,7 @@ class MoeWeights(ctypes.Structure):
 
 class MoeWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "sync", "logits", "gamma", "topk_ids", "topk_w", "union_ids", "union_count", "slot_to_union",
+        "sync", "logits", "score", "gamma", "topk_ids", "topk_w", "union_ids", "union_count", "slot_to_union",
         "row_mask", "slot_info", "act", "y", "total")]
 
 

@@ -133,8 +133,9 @@ void compute_layout(const moe_config* c, moe_ws_layout* L) {
     off = round_up(off + bytes, 256);
     return o;
   };
-  L->sync = take(sizeof(uint32_t));
+  L->sync = take(moe::kSyncBytes);
   L->logits = take(R * E * sizeof(float));
+  L->score = take(R * E * sizeof(double));
   L->gamma = take(R * sizeof(float));
   L->topk_ids = take(R * k * sizeof(int32_t));
   L->topk_w = take(R * k * sizeof(float));
@@ -192,6 +193,7 @@ void fill_route(moe::RouteParams& p, const moe_config* c, const moe_weights* w, 
   p.norm = c->norm_topk_prob;
   p.rsf = c->routed_scaling_factor;
   p.logits = reinterpret_cast<float*>(ws + L.logits);
+  p.score = reinterpret_cast<double*>(ws + L.score);
   p.gamma = reinterpret_cast<float*>(ws + L.gamma);
   p.ids_out = ids_out;
   p.w_out = w_out;

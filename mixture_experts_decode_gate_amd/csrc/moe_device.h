@@ -123,6 +123,28 @@ __device__ __forceinline__ double wave_sum(double v) {
   return __builtin_bit_cast(double, (hi << 32) | lo);
 }
 
+// wave_sum(double) of N independent values, step by step (same addition
+// order as wave_sum for every value).
+template <int N>
+__device__ __forceinline__ void wave_sum_n(double (&v)[N]) {
+#define MOE_SUM_STEP64(CTRL, MASK) \
+  _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] += dpp_f64<CTRL, MASK>(v[i]);
+  MOE_SUM_STEP64(0xB1, 0xF)
+  MOE_SUM_STEP64(0x4E, 0xF)
+  MOE_SUM_STEP64(0x141, 0xF)
+  MOE_SUM_STEP64(0x140, 0xF)
+  MOE_SUM_STEP64(0x142, 0xA)
+  MOE_SUM_STEP64(0x143, 0xC)
+#undef MOE_SUM_STEP64
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v[i]);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+    v[i] = __builtin_bit_cast(double, (hi << 32) | lo);
+  }
+}
+
 // Maximum over the 64 lanes (same DPP pattern as wave_sum; lanes a step
 // does not reach read 0, the identity), returned to every lane.
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {

@@ -10,6 +10,12 @@ namespace moe {
 
 struct SlotInfo;
 
+// Sync words at the start of the workspace: word 0 is the routing kernel's
+// arrival counter, zero between calls.
+constexpr size_t kSyncBytes = 256;
+constexpr int kDownGroup = 2;  // act rows a down segment carries
+constexpr int kMaxDownSegs = (MOE_MAX_IDS + 1) * ((MOE_MAX_ROWS + kDownGroup - 1) / kDownGroup);
+
 struct RouteParams {
   const uint16_t* x;       // [rows][h] bf16
   const float* router_w;   // [E][h]
@@ -19,6 +25,7 @@ struct RouteParams {
   int E, k, rows, route_kind, norm;
   float rsf;
   float* logits;           // [8][E]
+  double* score;           // [8][E] sigmoid(logit) in fp64 (sigmoid routing)
   float* gamma;            // [8]
   int32_t* ids_out;        // [rows][k]
   float* w_out;            // [rows][k]

@@ -30,7 +30,8 @@ namespace moe {
 // shared expert's gate vector): wave c < nkc takes the kRouterChunk-column
 // chunk c, issues all its loads before any arithmetic, accumulates in fp64
 // and reduces in a fixed order; the chunk partials are summed in chunk order
-// and rounded once: logits[r][e] = fp32(sum), gamma[r] = fp32(sigmoid(sum)).
+// and rounded once: logits[r][e] = fp32(sum), gamma[r] = fp32(sigmoid(sum)),
+// and for sigmoid routing score[r][e] = sigmoid(sum) in fp64.
 // Each block then publishes its results (device-scope fence) and takes a
 // ticket from the arrival counter; the block that draws the last ticket reads
 // every logit and runs top-k (one wave per row), the union (wave 0) and the
@@ -100,40 +101,47 @@ __device__ __forceinline__ float key_float(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
+// Weight pointers of the experts a top-k pass selected, by slot t = r*k + j,
+// gathered while the rest of the routing math runs.
+struct SlotPtrs {
+  const uint8_t* p[6];  // gate, up, down: packed codes then block scales
+  float scale2[3];
+};
+
 // Top-k of row r (one wave).  Lane l holds experts l*G .. l*G+G-1, so a lower
 // (lane, position) pair is a lower expert id.  Each of the k rounds takes the
 // lane's largest remaining key (lowest position on ties), the wave-wide
 // maximum of those, and the lowest lane holding it: the largest key, ties to
-// the lower id.  Weights follow in fp64.  Writes ids and weights of the row
-// to ids_out/w_out and the ids to s_ids.
+// the lower id.  Sigmoid keys are fp32(s) + bias with s the fp64 score the
+// router pass stored.  Weights follow in fp64.  Writes ids and weights of
+// the row to ids_out/w_out and the ids to s_ids; with tab != nullptr also
+// gathers the selected experts' weight pointers into tab (lane j < k loads
+// winner j's, so those loads overlap the weight math).
 template <int G>
-__device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids) {
+__device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids, SlotPtrs* tab) {
   const int E = p.E, k = p.k;
+  const bool softmax = p.route_kind == MOE_ROUTE_SOFTMAX;
   float lv[G], bv[G];
+  double sv[G];  // sigmoid score (sigmoid routing)
   // Every load first (clamped in-bounds indices, no branch) so they overlap.
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const int e = min(lane * G + i, E - 1);
     lv[i] = p.logits[r * E + e];
+    sv[i] = p.score[r * E + e];
     bv[i] = p.bias[e];
   }
-  const bool softmax = p.route_kind == MOE_ROUTE_SOFTMAX;
   uint32_t key[G];  // 0: not a candidate (past E, or already taken)
-  double sv[G];     // sigmoid score (sigmoid routing)
   int selj[G];      // round that took the expert, -1 if none
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const bool valid = lane * G + i < E;
-    float kf = lv[i];
-    sv[i] = 0.0;
-    if (!softmax && valid) {
-      sv[i] = 1.0 / (1.0 + exp(-(double)lv[i]));
-      kf = (float)sv[i] + bv[i];
-    }
+    const float kf = softmax ? lv[i] : (float)sv[i] + bv[i];
     key[i] = valid ? key_bits(kf) : 0u;
     selj[i] = -1;
   }
   float top_logit = 0.f;
+  int my_winner = 0;  // lane j: the expert taken in round j
   for (int j = 0; j < k; ++j) {
     uint32_t best = 0;
     int bi = 0;
@@ -159,10 +167,25 @@ __device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids) 
         }
     }
     if (j == 0) top_logit = key_float(m);  // softmax: the largest logit
+    if (lane == j) my_winner = be;
     if (lane == 0) {
       p.ids_out[r * k + j] = be;
       s_ids[r * k + j] = be;
     }
+  }
+  // Weight pointers of the winners, one winner per lane (k <= 64).
+  SlotPtrs sp;
+  if (tab != nullptr && lane < k) {
+    const int ex = my_winner;
+    sp.p[0] = p.gate.packed[ex];
+    sp.p[1] = p.gate.scales[ex];
+    sp.p[2] = p.up.packed[ex];
+    sp.p[3] = p.up.scales[ex];
+    sp.p[4] = p.down.packed[ex];
+    sp.p[5] = p.down.scales[ex];
+    sp.scale2[0] = p.gate.scale2[ex];
+    sp.scale2[1] = p.up.scale2[ex];
+    sp.scale2[2] = p.down.scale2[ex];
   }
   // Weights.  Softmax: exp(L - max), normalised over all experts, or over the
   // k selected when norm_topk_prob.  Sigmoid: s, optionally normalised over
@@ -171,13 +194,17 @@ __device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids) 
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     if (lane * G + i < E) {
-      if (softmax && (!p.norm || selj[i] >= 0)) sv[i] = exp((double)lv[i] - (double)top_logit);
-      all_part += sv[i];
-      if (selj[i] >= 0) sel_part += sv[i];
+      double v = sv[i];
+      if (softmax) v = (!p.norm || selj[i] >= 0) ? exp((double)lv[i] - (double)top_logit) : 0.0;
+      sv[i] = v;
+      all_part += v;
+      if (selj[i] >= 0) sel_part += v;
     }
   }
-  const double all_sum = softmax && !p.norm ? wave_sum(all_part) : 1.0;
-  const double sel_sum = p.norm ? wave_sum(sel_part) : 1.0;
+  double sums[2] = {all_part, sel_part};
+  wave_sum_n<2>(sums);
+  const double all_sum = softmax && !p.norm ? sums[0] : 1.0;
+  const double sel_sum = p.norm ? sums[1] : 1.0;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     if (selj[i] >= 0) {
@@ -191,12 +218,14 @@ __device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids) 
       p.w_out[r * k + selj[i]] = (float)wgt;
     }
   }
+  if (tab != nullptr && lane < k) tab[r * k + lane] = sp;
 }
 
 template <int R, int G>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int with_union) {
   __shared__ double part[kMaxRouterChunks][kMaxRows];
   __shared__ __align__(16) int32_t s_ids[kMaxIds];
+  __shared__ SlotPtrs s_tab[kMaxIds];
   __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -221,47 +250,74 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int
 #pragma unroll
       for (int r = 0; r < R; ++r) xv[r][it] = *reinterpret_cast<const uint2*>(p.x + (size_t)r * h + cc);
     }
+    double acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      double acc = 0.0;
+      acc[r] = 0.0;
 #pragma unroll
       for (int it = 0; it < kIt; ++it) {
         const double w0 = ok[it] ? (double)wv[it].x : 0.0, w1 = ok[it] ? (double)wv[it].y : 0.0;
         const double w2 = ok[it] ? (double)wv[it].z : 0.0, w3 = ok[it] ? (double)wv[it].w : 0.0;
-        acc = __builtin_fma((double)bf16_to_f32(xv[r][it].x & 0xFFFFu), w0, acc);
-        acc = __builtin_fma((double)bf16_to_f32(xv[r][it].x >> 16), w1, acc);
-        acc = __builtin_fma((double)bf16_to_f32(xv[r][it].y & 0xFFFFu), w2, acc);
-        acc = __builtin_fma((double)bf16_to_f32(xv[r][it].y >> 16), w3, acc);
+        acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].x & 0xFFFFu), w0, acc[r]);
+        acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].x >> 16), w1, acc[r]);
+        acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].y & 0xFFFFu), w2, acc[r]);
+        acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].y >> 16), w3, acc[r]);
       }
-      const double s = wave_sum(acc);
-      if (lane == 0) part[c][r] = s;
+    }
+    wave_sum_n<R>(acc);
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[c][r] = acc[r];
     }
   }
   __syncthreads();
-  // Thread 0 writes the block's results and takes a ticket with release
-  // order (its own stores become visible before the increment).  The block
-  // drawing the last ticket acquires, so its reads see every block's results.
-  // A full fence in every block would also invalidate every L2 on each
-  // arrival, which costs far more than the whole GEMV.
-  if (threadIdx.x == 0) {
+  // Wave 0: lane r sums row r's chunk partials in chunk order and takes the
+  // sigmoid (the gate row always; router rows for sigmoid routing).  Lane 0
+  // then writes every row's results and takes a ticket with release order
+  // (its own stores become visible before the increment).  The block drawing
+  // the last ticket acquires, so its reads see every block's results.  A full
+  // fence in every block would also invalidate every L2 on each arrival,
+  // which costs far more than the whole GEMV.
+  if (wave == 0) {
+    double z = 0.0, sg = 0.0;
+    if (lane < R) {
+      for (int cc = 0; cc < nkc; ++cc) z += part[cc][lane];
+      // The gate takes the fp64 sum; routing scores take the fp32 logit, the
+      // value top-k sees.
+      if (e == E)
+        sg = 1.0 / (1.0 + exp(-z));
+      else if (p.route_kind == MOE_ROUTE_SIGMOID_BIAS)
+        sg = 1.0 / (1.0 + exp(-(double)(float)z));
+    }
+    double zr[R], sr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      double z = 0.0;
-      for (int cc = 0; cc < nkc; ++cc) z += part[cc][r];
-      if (e < E)
-        p.logits[r * E + e] = (float)z;
-      else
-        p.gamma[r] = (float)(1.0 / (1.0 + exp(-z)));
+      const uint64_t zb = __builtin_bit_cast(uint64_t, z), sb = __builtin_bit_cast(uint64_t, sg);
+      zr[r] = __builtin_bit_cast(double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(zb >> 32), r) << 32) |
+                                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)zb, r));
+      sr[r] = __builtin_bit_cast(double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(sb >> 32), r) << 32) |
+                                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sb, r));
     }
-    const uint32_t ticket = __hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = ticket == gridDim.x - 1;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    s_last = last;
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (e < E) {
+          p.logits[r * E + e] = (float)zr[r];
+          p.score[r * E + e] = sr[r];
+        } else {
+          p.gamma[r] = (float)sr[r];
+        }
+      }
+      const uint32_t ticket = __hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = ticket == gridDim.x - 1;
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      s_last = last;
+    }
   }
   __syncthreads();
   if (!s_last) return;
 
-  if (wave < R) topk_row<G>(p, wave, lane, s_ids);
+  if (wave < R) topk_row<G>(p, wave, lane, s_ids, with_union ? s_tab : nullptr);
   if (with_union) {
     __syncthreads();
     if (wave == 0) {
@@ -269,20 +325,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int
       const int pos = union_wave(s_ids, R * p.k, p.k, R, lane, p.union_ids, p.union_count, p.slot_to_union,
                                  p.row_mask, &mask);
       if (pos >= 0) {
-        const int ex = s_ids[lane];
+        const SlotPtrs& t = s_tab[lane];  // lane is the union entry's first slot
         SlotInfo si;
-        si.gate_packed = p.gate.packed[ex];
-        si.gate_scales = p.gate.scales[ex];
-        si.up_packed = p.up.packed[ex];
-        si.up_scales = p.up.scales[ex];
-        si.down_packed = p.down.packed[ex];
-        si.down_scales = p.down.scales[ex];
-        si.gate_scale2 = p.gate.scale2[ex];
-        si.up_scale2 = p.up.scale2[ex];
-        si.down_scale2 = p.down.scale2[ex];
+        si.gate_packed = t.p[0];
+        si.gate_scales = t.p[1];
+        si.up_packed = t.p[2];
+        si.up_scales = t.p[3];
+        si.down_packed = t.p[4];
+        si.down_scales = t.p[5];
+        si.gate_scale2 = t.scale2[0];
+        si.up_scale2 = t.scale2[1];
+        si.down_scale2 = t.scale2[2];
         si.inter = p.inter;
         si.row_mask = mask;
-        si.expert = ex;
+        si.expert = s_ids[lane];
         p.slots[pos] = si;
       }
       if (lane == 0) {
@@ -400,7 +456,6 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   const int nwaves = blockDim.x >> 6;
   const int h = p.h;
   const int U = *p.union_count;
-  stage_rows<R, NCH>(xs, p.x, (size_t)h, h, (1u << R) - 1u);
   load_slot_table(s_slots, p.slots, U);
   __syncthreads();
 
@@ -462,18 +517,22 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     }
   };
 
-  if (cur.su > U) return;
-  // Three register buffers in rotation: while one item is computed, the next
-  // two are in flight.  Loads are always issued (a repeat of the last item
-  // past the end) so no branch separates them from the compute they overlap.
+  // The first two items' weights are requested before x is staged, so their
+  // latency overlaps the staging.  Waves without work still stage and sync.
+  const bool has_work = cur.su <= U;
   RowRegs<NCH> gc, uc;
   SlotInfo sc;
   int nc = 0, slot_c = 0;
   ItemCursor c1 = cur, c2 = cur;
   advance(c1, W, U, p.inter, p.shared_inter);
-  bool more1 = c1.su <= U;
-  fetch(cur, ga, ua, sa, na, slot_a);
-  fetch(more1 ? c1 : cur, gb, ub, sb, nb, slot_b);
+  bool more1 = has_work && c1.su <= U;
+  if (has_work) {
+    fetch(cur, ga, ua, sa, na, slot_a);
+    fetch(more1 ? c1 : cur, gb, ub, sb, nb, slot_b);
+  }
+  stage_rows<R, NCH>(xs, p.x, (size_t)h, h, (1u << R) - 1u);
+  __syncthreads();
+  if (!has_work) return;
   while (true) {
     c2 = more1 ? c1 : cur;
     advance(c2, W, U, p.inter, p.shared_inter);
@@ -510,6 +569,7 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
 //   y[slot][r][n] = W_down[n,:] . act[slot][r][:]
 constexpr int kDownThreads = 256;
 constexpr int kDownBatch = 4;  // weight rows per prefetch batch (stored as float4s)
+constexpr int kDownBufs = 3;   // batches in the prefetch rotation
 
 template <int NCH>
 struct DownBatch {
@@ -518,9 +578,8 @@ struct DownBatch {
 
 template <int R, int NCH>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
-  constexpr int kGroup = NCH == 1 ? 4 : 2;
-  constexpr int kGroupsPerSlot = (kMaxRows + kGroup - 1) / kGroup;
-  constexpr int kMaxSegs = kNumSlots * kGroupsPerSlot;
+  constexpr int kGroup = kDownGroup;  // act rows held per segment (16 VGPRs each per 2048 columns)
+  constexpr int kMaxSegs = kMaxDownSegs;
   __shared__ SlotInfo s_slots[kNumSlots];
   __shared__ int s_seg_slot[kMaxSegs];
   __shared__ uint32_t s_seg_rows[kMaxSegs];  // row i of the group in bits 4i..4i+3, count in bits 28..31
@@ -575,27 +634,29 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   }
   __syncthreads();
 
-  // Block b owns rows [N*b/B, N*(b+1)/B) of the segment row space; inside a
-  // segment its waves take interleaved batches of kDownBatch rows, so a block
-  // reads one contiguous window.
-  const long long N = (long long)s_nseg * h;
-  const long long b_begin = (N / kDownBatch) * blockIdx.x / gridDim.x * kDownBatch;
-  const long long b_end = (N / kDownBatch) * (blockIdx.x + 1) / gridDim.x * kDownBatch;
+  // Each segment gets a group of waves in proportion (virtual wave v of V
+  // works on segment v * nseg / V), and the group's waves take interleaved
+  // batches of kDownBatch rows: every group sweeps its matrix front to back
+  // together.  With fewer waves than segments a wave takes several virtual
+  // waves in turn.
+  const int W = gridDim.x * nwaves;
+  const int nseg = s_nseg;
+  const int V = W > nseg ? W : nseg;
 
-  DownBatch<NCH> A, B;
+  DownBatch<NCH> buf[kDownBufs];
   u32x4 act[kGroup][NCH][4];
-  for (long long pos = b_begin; pos < b_end;) {
-    const int seg = (int)(pos / h);
-    const int n_begin = (int)(pos - (long long)seg * h);
-    const int n_end = (int)(((long long)seg + 1) * h < b_end ? h : b_end - (long long)seg * h);
-    pos += n_end - n_begin;
+  for (int v = blockIdx.x * nwaves + wave; v < V; v += W) {
+    const int seg = (int)((long long)v * nseg / V);
+    const int first = (int)(((long long)V * seg + nseg - 1) / nseg);  // first virtual wave of the segment
+    const int last = (int)(((long long)V * (seg + 1) + nseg - 1) / nseg);
+    const int n_end = h;
     const int slot = s_seg_slot[seg];
     const uint32_t rows = s_seg_rows[seg];
     const int cnt = (int)(rows >> 28);
     const SlotInfo& si = s_slots[slot];
     const int K = si.inter;
-    const int stride = nwaves * kDownBatch;
-    int n0 = n_begin + wave * kDownBatch;
+    const int stride = (last - first) * kDownBatch;
+    const int n0 = (v - first) * kDownBatch;
     if (n0 >= n_end) continue;
     // act rows of the group (unused entries repeat the last row).  Lanes past
     // K read the row's first columns: finite values that meet zeroed scales.
@@ -663,17 +724,25 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
         }
       }
     };
-    fetch(n0, A);
-    while (true) {
-      const int n1 = n0 + stride;
-      fetch(n1 < n_end ? n1 : n0, B);
-      compute(n0, A);
-      if (n1 >= n_end) break;
-      const int n2 = n1 + stride;
-      fetch(n2 < n_end ? n2 : n1, A);
-      compute(n1, B);
-      if (n2 >= n_end) break;
-      n0 = n2;
+    // kDownBufs batches in rotation: while one is computed, the next
+    // kDownBufs - 1 are in flight.  Batches past the range reload the last
+    // row (no branch around the loads) and are not computed.
+    int nf = n0;  // next batch to fetch
+#pragma unroll
+    for (int i = 0; i < kDownBufs - 1; ++i) {
+      fetch(nf < n_end ? nf : n_end - 1, buf[i]);
+      nf += stride;
+    }
+    for (int nc = n0;;) {
+#pragma unroll
+      for (int i = 0; i < kDownBufs; ++i) {
+        fetch(nf < n_end ? nf : n_end - 1, buf[(i + kDownBufs - 1) % kDownBufs]);
+        nf += stride;
+        compute(nc, buf[i]);
+        nc += stride;
+        if (nc >= n_end) break;
+      }
+      if (nc >= n_end) break;
     }
   }
 }

@@ -62,6 +62,8 @@ def run_forward(dl, x_bits: np.ndarray, ws=None):
     ws = ws_for(dl.cfg) if ws is None else ws
     moe.moe_forward(dl.cfg, dl.weights, x, out, ws)
     torch.cuda.synchronize()
+    # the routing kernel's arrival counter is back at zero after every call
+    assert ws_read(ws, moe.moe_workspace_layout(dl.cfg).sync, np.uint32, 1)[0] == 0
     return out_bits(out), ws
 
 
