@@ -426,52 +426,53 @@ __device__ __forceinline__ void load_row(RowRegs<NCH>& b, const uint8_t* packed,
   }
 }
 
-// Position in the flattened gate/up work list: union slot index (U means the
-// shared expert) and row n.  Advancing by a stride walks the routed slots'
-// I rows each, then the shared expert's Is rows.
-struct ItemCursor {
-  int su;  // 0..U-1 routed, U shared, > U done
-  int n;
-};
-
-__device__ __forceinline__ void advance(ItemCursor& c, int step, int U, int inter, int shared_inter) {
-  c.n += step;
-  while (c.su <= U) {
-    const int rows = c.su < U ? inter : shared_inter;
-    if (c.n < rows) break;
-    c.n -= rows;
-    ++c.su;
-  }
-}
-
 // Gate+up sweep.  Work items are rows n of each union slot's gate and up
-// matrices, dealt round-robin to every wave of the grid; a wave loads its next
-// item while it computes the current one.  For each row r that uses the slot:
+// matrices (routed slots' I rows each, then the shared expert's Is rows).
+// Block b owns items b, b + B, b + 2B, ... (B blocks), so all blocks sweep
+// the weights front to back together; its waves claim the block's items in
+// order from a counter in LDS.  Waves that share a SIMD are not issued evenly
+// (the oldest goes first): with claims, one that is issued less simply takes
+// fewer items, instead of finishing far behind its neighbours.  A claim is an
+// LDS atomic, tracked apart from the weight loads, so taking one never waits
+// for prefetched weights.  A wave loads its next items while it computes the
+// current one.  For each row r that uses the slot:
 //   act[slot][r][n] = bf16(silu(g) * v), g = W_gate[n,:] . x_r, v = W_up[n,:] . x_r.
 template <int R, int NCH>
 __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p) {
   extern __shared__ u32x4 xs[];  // [R][NCH][256] staged x rows
   __shared__ SlotInfo s_slots[kNumSlots];
+  __shared__ int s_next;  // the block's next unclaimed item
   const int lane = threadIdx.x & 63;
-  const int nwaves = blockDim.x >> 6;
   const int h = p.h;
   const int U = *p.union_count;
+  if (threadIdx.x == 0) s_next = 0;
   load_slot_table(s_slots, p.slots, U);
   __syncthreads();
 
-  const int W = gridDim.x * nwaves;
-  ItemCursor cur{0, 0};
-  advance(cur, blockIdx.x * nwaves + wave_id(), U, p.inter, p.shared_inter);
-
-  auto slot_of = [&](int su) { return su < U ? su : kSharedSlot; };
+  const int routed_items = U * p.inter;
+  const int total = routed_items + p.shared_inter;
+  // Item id of the block's next claim, or -1 once the block's items run out
+  // (claims only grow, so every later claim fails too).
+  auto claim = [&]() -> int {
+    int i = 0;
+    if (lane == 0) i = atomicAdd(&s_next, 1);
+    i = __builtin_amdgcn_readfirstlane(i);
+    const long long id = (long long)blockIdx.x + (long long)i * gridDim.x;
+    return id < total ? (int)id : -1;
+  };
   RowRegs<NCH> ga, ua, gb, ub;
   SlotInfo sa, sb;
   int na = 0, nb = 0, slot_a = 0, slot_b = 0;
 
-  auto fetch = [&](const ItemCursor& c, RowRegs<NCH>& g, RowRegs<NCH>& u, SlotInfo& si, int& n, int& slot) {
-    slot = slot_of(c.su);
+  auto fetch = [&](int id, RowRegs<NCH>& g, RowRegs<NCH>& u, SlotInfo& si, int& n, int& slot) {
+    if (id < routed_items) {
+      slot = id / p.inter;
+      n = id - slot * p.inter;
+    } else {
+      slot = kSharedSlot;
+      n = id - routed_items;
+    }
     si = s_slots[slot];
-    n = c.n;
     load_row<NCH>(g, si.gate_packed, si.gate_scales, n, h, lane);
     load_row<NCH>(u, si.up_packed, si.up_scales, n, h, lane);
   };
@@ -517,45 +518,40 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     }
   };
 
-  // The first two items' weights are requested before x is staged, so their
-  // latency overlaps the staging.  Waves without work still stage and sync.
-  const bool has_work = cur.su <= U;
+  // Three register buffers in rotation: while one item is computed, the next
+  // two are in flight.  Loads are always issued (a valid item repeated once
+  // the claims run out) so no branch separates them from the compute they
+  // overlap.  The first two items' weights are requested before x is staged,
+  // so their latency overlaps the staging; waves without work still stage and
+  // sync.
   RowRegs<NCH> gc, uc;
   SlotInfo sc;
   int nc = 0, slot_c = 0;
-  ItemCursor c1 = cur, c2 = cur;
-  advance(c1, W, U, p.inter, p.shared_inter);
-  bool more1 = has_work && c1.su <= U;
+  int id_a = claim();
+  const bool has_work = id_a >= 0;
+  int id_b = has_work ? claim() : -1;
   if (has_work) {
-    fetch(cur, ga, ua, sa, na, slot_a);
-    fetch(more1 ? c1 : cur, gb, ub, sb, nb, slot_b);
+    fetch(id_a, ga, ua, sa, na, slot_a);
+    fetch(id_b >= 0 ? id_b : id_a, gb, ub, sb, nb, slot_b);
   }
   stage_rows<R, NCH>(xs, p.x, (size_t)h, h, (1u << R) - 1u);
   __syncthreads();
   if (!has_work) return;
   while (true) {
-    c2 = more1 ? c1 : cur;
-    advance(c2, W, U, p.inter, p.shared_inter);
-    bool more2 = more1 && c2.su <= U;
-    fetch(more2 ? c2 : cur, gc, uc, sc, nc, slot_c);
+    const int id_c = id_b >= 0 ? claim() : -1;
+    fetch(id_c >= 0 ? id_c : id_a, gc, uc, sc, nc, slot_c);
     compute(ga, ua, sa, na, slot_a);
-    if (!more1) break;
-    // rotate: b -> a role
-    ItemCursor c3 = more2 ? c2 : cur;
-    advance(c3, W, U, p.inter, p.shared_inter);
-    bool more3 = more2 && c3.su <= U;
-    fetch(more3 ? c3 : cur, ga, ua, sa, na, slot_a);
+    if (id_b < 0) break;
+    const int id_a2 = id_c >= 0 ? claim() : -1;
+    fetch(id_a2 >= 0 ? id_a2 : id_b, ga, ua, sa, na, slot_a);
     compute(gb, ub, sb, nb, slot_b);
-    if (!more2) break;
-    ItemCursor c4 = more3 ? c3 : cur;
-    advance(c4, W, U, p.inter, p.shared_inter);
-    bool more4 = more3 && c4.su <= U;
-    fetch(more4 ? c4 : cur, gb, ub, sb, nb, slot_b);
+    if (id_c < 0) break;
+    const int id_b2 = id_a2 >= 0 ? claim() : -1;
+    fetch(id_b2 >= 0 ? id_b2 : id_c, gb, ub, sb, nb, slot_b);
     compute(gc, uc, sc, nc, slot_c);
-    if (!more3) break;
-    cur = c3;
-    c1 = c4;
-    more1 = more4;
+    if (id_a2 < 0) break;
+    id_a = id_a2;
+    id_b = id_b2;
   }
 }
 
