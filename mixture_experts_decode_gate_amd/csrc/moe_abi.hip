@@ -247,10 +247,11 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
   sp.act_stride = cfg->moe_inter > cfg->shared_inter ? cfg->moe_inter : cfg->shared_inter;
   sp.inter = cfg->moe_inter;
   sp.shared_inter = cfg->shared_inter;
+  sp.route = rp;
 
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return device_status(e, "event record");
-  if ((e = moe::launch_route(rp, true, s)) != hipSuccess) return device_status(e, "route launch");
+  if ((e = moe::launch_route(rp, false, s)) != hipSuccess) return device_status(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return device_status(e, "event record");
   if ((e = moe::launch_gateup(sp, rows, max_union, s)) != hipSuccess) return device_status(e, "gate/up launch");
   if ((e = mark(2)) != hipSuccess) return device_status(e, "event record");
@@ -301,7 +302,7 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   moe::RouteParams rp;
   fill_route(rp, cfg, w, x_bf16, rows, wsb, L, topk_ids, topk_w);
-  hipError_t e = moe::launch_route(rp, false, s);
+  hipError_t e = moe::launch_route(rp, true, s);
   if (e != hipSuccess) return device_status(e, "route launch");
   return ok();
 }

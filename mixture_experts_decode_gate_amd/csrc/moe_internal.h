@@ -43,19 +43,20 @@ struct RouteParams {
 
 struct SweepParams {
   const uint16_t* x;          // [rows][h] bf16
-  const SlotInfo* slots;      // [65]
-  const int32_t* union_count; // device U
+  const SlotInfo* slots;      // [65] (down sweep; written by the gate/up sweep)
+  const int32_t* union_count; // device U (down sweep)
   uint16_t* act;              // [65][8][act_stride] bf16
   float* y;                   // [65][8][h] fp32
   int h;
   int act_stride;             // max(inter, shared_inter)
   int inter;                  // routed expert intermediate size
   int shared_inter;
+  RouteParams route;          // the gate/up sweep takes top-k from route.logits / route.score
 };
 
 constexpr size_t kSlotInfoBytes = 72;  // sizeof(SlotInfo), checked in the kernels file
 
-hipError_t launch_route(const RouteParams& p, bool with_union, hipStream_t s);
+hipError_t launch_route(const RouteParams& p, bool do_topk, hipStream_t s);
 hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids, int32_t* union_count,
                         int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);
 hipError_t launch_gateup(const SweepParams& p, int rows, int max_union, hipStream_t s);

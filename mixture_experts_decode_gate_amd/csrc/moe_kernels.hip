@@ -24,7 +24,9 @@
 namespace moe {
 
 // ---------------------------------------------------------------- routing
-// One kernel: router GEMV, top-k, union and slot resolution.
+// Router GEMV, and for moe_route top-k in the same kernel.  moe_forward runs
+// the GEMV alone; every gate/up block then takes top-k, the union and the
+// slot table itself from the stored logits (see the gate/up sweep).
 //
 // Block e (of E+1) computes router row e for every input row (e == E is the
 // shared expert's gate vector): wave c < nkc takes the kRouterChunk-column
@@ -32,10 +34,10 @@ namespace moe {
 // and reduces in a fixed order; the chunk partials are summed in chunk order
 // and rounded once: logits[r][e] = fp32(sum), gamma[r] = fp32(sigmoid(sum)),
 // and for sigmoid routing score[r][e] = sigmoid(sum) in fp64.
-// Each block then publishes its results (device-scope fence) and takes a
-// ticket from the arrival counter; the block that draws the last ticket reads
-// every logit and runs top-k (one wave per row), the union (wave 0) and the
-// slot resolution, then resets the counter to zero for the next call.
+// With top-k each block then publishes its results and takes a ticket from
+// the arrival counter; the block that draws the last ticket reads every logit
+// and runs top-k (one wave per row), then resets the counter to zero for the
+// next call.
 constexpr int kRouterChunk = 1024;
 constexpr int kMaxRouterChunks = MOE_MAX_DIM / kRouterChunk;
 constexpr int kRouteThreads = 64 * kMaxRows;  // >= one wave per row for top-k, >= nkc waves
@@ -46,9 +48,12 @@ static_assert(MOE_MAX_EXPERTS <= 64 * 16, "top-k holds at most 16 keys per lane"
 // id with every slot at once (broadcast LDS reads, no sort): slot t is a first
 // occurrence when no earlier slot holds its id.  First occurrences, in slot
 // order, form the union.  Returns the lane's union position if it is a first
-// occurrence (else -1) and, in *mask_out, the rows that chose its id.
+// occurrence (else -1), in *mask_out the rows that chose its id and in
+// *count_out the union size U.  The union outputs are written when
+// union_ids is not null (row_mask may be null on its own).
 __device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows, int lane, int32_t* union_ids,
-                          int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask, uint32_t* mask_out) {
+                          int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask, uint32_t* mask_out,
+                          int* count_out) {
   const int id = lane < n ? ids_lds[lane] : -1;
   uint64_t eq = 0;
 #pragma unroll
@@ -69,13 +74,16 @@ __device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows, int la
   const unsigned long long bal = __ballot(is_first);
   const int pos_self = __popcll(bal & ((1ull << lane) - 1ull));
   const int pos_first = __popcll(bal & ((1ull << first) - 1ull));
-  if (lane < n) slot_to_union[lane] = pos_first;
-  if (is_first) {
-    union_ids[pos_self] = id;
-    if (row_mask) row_mask[pos_self] = mask;
+  if (union_ids != nullptr) {
+    if (lane < n) slot_to_union[lane] = pos_first;
+    if (is_first) {
+      union_ids[pos_self] = id;
+      if (row_mask) row_mask[pos_self] = mask;
+    }
+    if (lane == 0) *union_count = __popcll(bal);
   }
-  if (lane == 0) *union_count = __popcll(bal);
   *mask_out = mask;
+  *count_out = __popcll(bal);
   return is_first ? pos_self : -1;
 }
 
@@ -88,7 +96,8 @@ __global__ __launch_bounds__(64) void union_kernel(const int32_t* __restrict__ i
   s_ids[lane] = lane < n ? ids[lane] : -1;
   __syncthreads();
   uint32_t mask;
-  union_wave(s_ids, n, k, rows, lane, union_ids, union_count, slot_to_union, row_mask, &mask);
+  int count;
+  union_wave(s_ids, n, k, rows, lane, union_ids, union_count, slot_to_union, row_mask, &mask, &count);
 }
 
 // Order-preserving map of a float key to uint32 (larger float -> larger
@@ -101,9 +110,8 @@ __device__ __forceinline__ float key_float(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-// Weight pointers of the experts a top-k pass selected, by slot t = r*k + j,
-// gathered while the rest of the routing math runs.
-struct SlotPtrs {
+// Weight pointers of one expert, staged in LDS by the block that runs top-k.
+struct ExpertPtrs {
   const uint8_t* p[6];  // gate, up, down: packed codes then block scales
   float scale2[3];
 };
@@ -113,12 +121,10 @@ struct SlotPtrs {
 // lane's largest remaining key (lowest position on ties), the wave-wide
 // maximum of those, and the lowest lane holding it: the largest key, ties to
 // the lower id.  Sigmoid keys are fp32(s) + bias with s the fp64 score the
-// router pass stored.  Weights follow in fp64.  Writes ids and weights of
-// the row to ids_out/w_out and the ids to s_ids; with tab != nullptr also
-// gathers the selected experts' weight pointers into tab (lane j < k loads
-// winner j's, so those loads overlap the weight math).
+// router pass stored.  Writes the row's ids to s_ids; with publish also its
+// ids and weights (fp64, rounded once) to ids_out/w_out.
 template <int G>
-__device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids, SlotPtrs* tab) {
+__device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids, bool publish) {
   const int E = p.E, k = p.k;
   const bool softmax = p.route_kind == MOE_ROUTE_SOFTMAX;
   float lv[G], bv[G];
@@ -141,7 +147,6 @@ __device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids, 
     selj[i] = -1;
   }
   float top_logit = 0.f;
-  int my_winner = 0;  // lane j: the expert taken in round j
   for (int j = 0; j < k; ++j) {
     uint32_t best = 0;
     int bi = 0;
@@ -167,26 +172,12 @@ __device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids, 
         }
     }
     if (j == 0) top_logit = key_float(m);  // softmax: the largest logit
-    if (lane == j) my_winner = be;
     if (lane == 0) {
-      p.ids_out[r * k + j] = be;
+      if (publish) p.ids_out[r * k + j] = be;
       s_ids[r * k + j] = be;
     }
   }
-  // Weight pointers of the winners, one winner per lane (k <= 64).
-  SlotPtrs sp;
-  if (tab != nullptr && lane < k) {
-    const int ex = my_winner;
-    sp.p[0] = p.gate.packed[ex];
-    sp.p[1] = p.gate.scales[ex];
-    sp.p[2] = p.up.packed[ex];
-    sp.p[3] = p.up.scales[ex];
-    sp.p[4] = p.down.packed[ex];
-    sp.p[5] = p.down.scales[ex];
-    sp.scale2[0] = p.gate.scale2[ex];
-    sp.scale2[1] = p.up.scale2[ex];
-    sp.scale2[2] = p.down.scale2[ex];
-  }
+  if (!publish) return;
   // Weights.  Softmax: exp(L - max), normalised over all experts, or over the
   // k selected when norm_topk_prob.  Sigmoid: s, optionally normalised over
   // the selected, times routed_scaling_factor.
@@ -218,14 +209,12 @@ __device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids, 
       p.w_out[r * k + selj[i]] = (float)wgt;
     }
   }
-  if (tab != nullptr && lane < k) tab[r * k + lane] = sp;
 }
 
 template <int R, int G>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int with_union) {
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int do_topk) {
   __shared__ double part[kMaxRouterChunks][kMaxRows];
   __shared__ __align__(16) int32_t s_ids[kMaxIds];
-  __shared__ SlotPtrs s_tab[kMaxIds];
   __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -272,12 +261,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int
   }
   __syncthreads();
   // Wave 0: lane r sums row r's chunk partials in chunk order and takes the
-  // sigmoid (the gate row always; router rows for sigmoid routing).  Lane 0
-  // then writes every row's results and takes a ticket with release order
-  // (its own stores become visible before the increment).  The block drawing
-  // the last ticket acquires, so its reads see every block's results.  A full
-  // fence in every block would also invalidate every L2 on each arrival,
-  // which costs far more than the whole GEMV.
+  // sigmoid (the gate row always; router rows for sigmoid routing), and lane
+  // 0 writes every row's results.  Without top-k that is all: the kernel that
+  // follows reads them after the kernel boundary.  With top-k, lane 0 takes a
+  // ticket with release order (its own stores become visible before the
+  // increment), and the block drawing the last ticket acquires, so its reads
+  // see every block's results.  A full fence in every block would also
+  // invalidate every L2 on each arrival, which costs far more than the GEMV.
   if (wave == 0) {
     double z = 0.0, sg = 0.0;
     if (lane < R) {
@@ -308,57 +298,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int
           p.gamma[r] = (float)sr[r];
         }
       }
+    }
+    if (do_topk && lane == 0) {
       const uint32_t ticket = __hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       const bool last = ticket == gridDim.x - 1;
       if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       s_last = last;
     }
   }
+  if (!do_topk) return;  // the next kernel runs top-k on these results
   __syncthreads();
   if (!s_last) return;
 
-  if (wave < R) topk_row<G>(p, wave, lane, s_ids, with_union ? s_tab : nullptr);
-  if (with_union) {
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t mask;
-      const int pos = union_wave(s_ids, R * p.k, p.k, R, lane, p.union_ids, p.union_count, p.slot_to_union,
-                                 p.row_mask, &mask);
-      if (pos >= 0) {
-        const SlotPtrs& t = s_tab[lane];  // lane is the union entry's first slot
-        SlotInfo si;
-        si.gate_packed = t.p[0];
-        si.gate_scales = t.p[1];
-        si.up_packed = t.p[2];
-        si.up_scales = t.p[3];
-        si.down_packed = t.p[4];
-        si.down_scales = t.p[5];
-        si.gate_scale2 = t.scale2[0];
-        si.up_scale2 = t.scale2[1];
-        si.down_scale2 = t.scale2[2];
-        si.inter = p.inter;
-        si.row_mask = mask;
-        si.expert = s_ids[lane];
-        p.slots[pos] = si;
-      }
-      if (lane == 0) {
-        SlotInfo si;
-        si.gate_packed = p.shared_gate.packed;
-        si.gate_scales = p.shared_gate.scales;
-        si.up_packed = p.shared_up.packed;
-        si.up_scales = p.shared_up.scales;
-        si.down_packed = p.shared_down.packed;
-        si.down_scales = p.shared_down.scales;
-        si.gate_scale2 = p.shared_gate.scale2;
-        si.up_scale2 = p.shared_up.scale2;
-        si.down_scale2 = p.shared_down.scale2;
-        si.inter = p.shared_inter;
-        si.row_mask = (1u << R) - 1u;
-        si.expert = -1;
-        p.slots[kSharedSlot] = si;
-      }
-    }
-  }
+  if (wave < R) topk_row<G>(p, wave, lane, s_ids, true);
   // every other block has arrived: reset for the next call
   if (threadIdx.x == 0) __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -426,8 +378,47 @@ __device__ __forceinline__ void load_row(RowRegs<NCH>& b, const uint8_t* packed,
   }
 }
 
-// Gate+up sweep.  Work items are rows n of each union slot's gate and up
-// matrices (routed slots' I rows each, then the shared expert's Is rows).
+// Weight pointers of union slot `slot` for expert ex (ex < 0: the shared
+// expert, used by every row).
+__device__ __forceinline__ SlotInfo slot_info(const RouteParams& rp, int ex, uint32_t row_mask) {
+  SlotInfo si;
+  if (ex >= 0) {
+    si.gate_packed = rp.gate.packed[ex];
+    si.gate_scales = rp.gate.scales[ex];
+    si.up_packed = rp.up.packed[ex];
+    si.up_scales = rp.up.scales[ex];
+    si.down_packed = rp.down.packed[ex];
+    si.down_scales = rp.down.scales[ex];
+    si.gate_scale2 = rp.gate.scale2[ex];
+    si.up_scale2 = rp.up.scale2[ex];
+    si.down_scale2 = rp.down.scale2[ex];
+    si.inter = rp.inter;
+  } else {
+    si.gate_packed = rp.shared_gate.packed;
+    si.gate_scales = rp.shared_gate.scales;
+    si.up_packed = rp.shared_up.packed;
+    si.up_scales = rp.shared_up.scales;
+    si.down_packed = rp.shared_down.packed;
+    si.down_scales = rp.shared_down.scales;
+    si.gate_scale2 = rp.shared_gate.scale2;
+    si.up_scale2 = rp.shared_up.scale2;
+    si.down_scale2 = rp.shared_down.scale2;
+    si.inter = rp.shared_inter;
+  }
+  si.row_mask = row_mask;
+  si.expert = ex;
+  return si;
+}
+
+// Gate+up sweep.  It starts with the routing decisions: every block runs
+// top-k on the logits the router pass stored (one wave per row), the union
+// and the slot table, all in LDS; block 0 also writes them to the workspace
+// for the down sweep and the blend.  Redundant work in every block costs a
+// few microseconds of arithmetic on 24 KB of L2 reads, against a grid-wide
+// hand-off that would cost a ticket, fences and an extra memory round trip.
+//
+// Work items are rows n of each union slot's gate and up matrices (the shared
+// expert's Is rows first, then each routed slot's I rows).
 // Block b owns items b, b + B, b + 2B, ... (B blocks), so all blocks sweep
 // the weights front to back together; its waves claim the block's items in
 // order from a counter in LDS.  Waves that share a SIMD are not issued evenly
@@ -437,44 +428,78 @@ __device__ __forceinline__ void load_row(RowRegs<NCH>& b, const uint8_t* packed,
 // for prefetched weights.  A wave loads its next items while it computes the
 // current one.  For each row r that uses the slot:
 //   act[slot][r][n] = bf16(silu(g) * v), g = W_gate[n,:] . x_r, v = W_up[n,:] . x_r.
-template <int R, int NCH>
+template <int R, int NCH, int G>
 __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p) {
   extern __shared__ u32x4 xs[];  // [R][NCH][256] staged x rows
   __shared__ SlotInfo s_slots[kNumSlots];
+  __shared__ __align__(16) int32_t s_ids[kMaxIds];
   __shared__ int s_next;  // the block's next unclaimed item
+  __shared__ int s_union;
   const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
   const int h = p.h;
-  const int U = *p.union_count;
-  if (threadIdx.x == 0) s_next = 0;
-  load_slot_table(s_slots, p.slots, U);
+  const RouteParams& rp = p.route;
+  const bool publish = blockIdx.x == 0;
+  if (threadIdx.x == 0) {
+    s_next = 0;
+    const SlotInfo si = slot_info(rp, -1, (1u << R) - 1u);
+    s_slots[kSharedSlot] = si;
+    if (publish) rp.slots[kSharedSlot] = si;
+  }
   __syncthreads();
 
-  const int routed_items = U * p.inter;
-  const int total = routed_items + p.shared_inter;
-  // Item id of the block's next claim, or -1 once the block's items run out
-  // (claims only grow, so every later claim fails too).
-  auto claim = [&]() -> int {
+  // Items: the shared expert's Is rows first, then each routed slot's I rows.
+  // The item id of the block's claim i is b + i * B (not yet checked against
+  // the item count, which needs U).
+  auto claim_id = [&]() -> long long {
     int i = 0;
     if (lane == 0) i = atomicAdd(&s_next, 1);
     i = __builtin_amdgcn_readfirstlane(i);
-    const long long id = (long long)blockIdx.x + (long long)i * gridDim.x;
-    return id < total ? (int)id : -1;
+    return (long long)blockIdx.x + (long long)i * gridDim.x;
   };
   RowRegs<NCH> ga, ua, gb, ub;
   SlotInfo sa, sb;
   int na = 0, nb = 0, slot_a = 0, slot_b = 0;
-
   auto fetch = [&](int id, RowRegs<NCH>& g, RowRegs<NCH>& u, SlotInfo& si, int& n, int& slot) {
-    if (id < routed_items) {
-      slot = id / p.inter;
-      n = id - slot * p.inter;
-    } else {
+    if (id < p.shared_inter) {
       slot = kSharedSlot;
-      n = id - routed_items;
+      n = id;
+    } else {
+      slot = (id - p.shared_inter) / p.inter;
+      n = id - p.shared_inter - slot * p.inter;
     }
     si = s_slots[slot];
     load_row<NCH>(g, si.gate_packed, si.gate_scales, n, h, lane);
     load_row<NCH>(u, si.up_packed, si.up_scales, n, h, lane);
+  };
+  // A first claim on a shared-expert row needs no routing: its weights are
+  // requested now and arrive while the block runs top-k.
+  long long first = claim_id();
+  const bool early = first < p.shared_inter;
+  if (early) fetch((int)first, ga, ua, sa, na, slot_a);
+
+  if (wave < R) topk_row<G>(rp, wave, lane, s_ids, publish);
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t mask;
+    int count;
+    const int pos = union_wave(s_ids, R * rp.k, rp.k, R, lane, publish ? rp.union_ids : nullptr, rp.union_count,
+                               rp.slot_to_union, rp.row_mask, &mask, &count);
+    if (pos >= 0) {  // lane is the union entry's first slot
+      const SlotInfo si = slot_info(rp, s_ids[lane], mask);
+      s_slots[pos] = si;
+      if (publish) rp.slots[pos] = si;
+    }
+    if (lane == 0) s_union = count;
+  }
+  __syncthreads();
+  const int U = s_union;
+  const long long total = (long long)p.shared_inter + (long long)U * p.inter;
+  // Item id of the block's next claim, or -1 once the block's items run out
+  // (claims only grow, so every later claim fails too).
+  auto claim = [&]() -> int {
+    const long long id = claim_id();
+    return id < total ? (int)id : -1;
   };
 
   auto compute = [&](const RowRegs<NCH>& g, const RowRegs<NCH>& u, const SlotInfo& si, int n, int slot) {
@@ -527,11 +552,11 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   RowRegs<NCH> gc, uc;
   SlotInfo sc;
   int nc = 0, slot_c = 0;
-  int id_a = claim();
+  int id_a = first < total ? (int)first : -1;
   const bool has_work = id_a >= 0;
   int id_b = has_work ? claim() : -1;
   if (has_work) {
-    fetch(id_a, ga, ua, sa, na, slot_a);
+    if (!early) fetch(id_a, ga, ua, sa, na, slot_a);
     fetch(id_b >= 0 ? id_b : id_a, gb, ub, sb, nb, slot_b);
   }
   stage_rows<R, NCH>(xs, p.x, (size_t)h, h, (1u << R) - 1u);
@@ -812,32 +837,38 @@ dim3 sweep_grid(K kernel, size_t lds, int max_blocks, SweepShape& cache, int def
 }
 
 template <int R>
-hipError_t route_r(const RouteParams& p, bool with_union, hipStream_t s) {
+hipError_t route_r(const RouteParams& p, bool do_topk, hipStream_t s) {
   // keys per lane: 4 covers up to 256 experts, 16 up to MOE_MAX_EXPERTS
   if (p.E <= 256)
-    hipLaunchKernelGGL((route_kernel<R, 4>), dim3(p.E + 1), dim3(kRouteThreads), 0, s, p, (int)with_union);
+    hipLaunchKernelGGL((route_kernel<R, 4>), dim3(p.E + 1), dim3(kRouteThreads), 0, s, p, (int)do_topk);
   else
-    hipLaunchKernelGGL((route_kernel<R, 16>), dim3(p.E + 1), dim3(kRouteThreads), 0, s, p, (int)with_union);
+    hipLaunchKernelGGL((route_kernel<R, 16>), dim3(p.E + 1), dim3(kRouteThreads), 0, s, p, (int)do_topk);
+  return hipGetLastError();
+}
+
+template <int R, int NCH, int G>
+hipError_t gateup_rng(const SweepParams& p, int max_items, hipStream_t s) {
+  const size_t lds = (size_t)R * NCH * kChunkUnits * 16;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)gateup_kernel<R, NCH, G>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  static SweepShape shape;
+  const dim3 grid = sweep_grid(gateup_kernel<R, NCH, G>, lds, 1 << 30, shape, 512);
+  const int waves = (int)grid.x * (shape.threads / 64);
+  dim3 g = grid;
+  if (waves > max_items) g.x = (max_items * 64 + shape.threads - 1) / shape.threads;
+  hipLaunchKernelGGL((gateup_kernel<R, NCH, G>), g, dim3(shape.threads), lds, s, p);
   return hipGetLastError();
 }
 
 template <int R, int NCH>
 hipError_t gateup_rn(const SweepParams& p, int max_items, hipStream_t s) {
-  const size_t lds = (size_t)R * NCH * kChunkUnits * 16;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e =
-        hipFuncSetAttribute((const void*)gateup_kernel<R, NCH>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  static SweepShape shape;
-  const dim3 grid = sweep_grid(gateup_kernel<R, NCH>, lds, 1 << 30, shape, 512);
-  const int waves = (int)grid.x * (shape.threads / 64);
-  dim3 g = grid;
-  if (waves > max_items) g.x = (max_items * 64 + shape.threads - 1) / shape.threads;
-  hipLaunchKernelGGL((gateup_kernel<R, NCH>), g, dim3(shape.threads), lds, s, p);
-  return hipGetLastError();
+  // top-k keys per lane: 4 covers up to 256 experts, 16 up to MOE_MAX_EXPERTS
+  return p.route.E <= 256 ? gateup_rng<R, NCH, 4>(p, max_items, s) : gateup_rng<R, NCH, 16>(p, max_items, s);
 }
 
 template <int R, int NCH>
@@ -879,11 +910,11 @@ hipError_t down_r(const SweepParams& p, int nch, int max_union, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_route(const RouteParams& p, bool with_union, hipStream_t s) {
+hipError_t launch_route(const RouteParams& p, bool do_topk, hipStream_t s) {
   switch (p.rows) {
 #define MOE_ROUTE_CASE(R) \
   case R:                 \
-    return route_r<R>(p, with_union, s);
+    return route_r<R>(p, do_topk, s);
     MOE_ROUTE_CASE(1)
     MOE_ROUTE_CASE(2)
     MOE_ROUTE_CASE(3)
