@@ -153,6 +153,7 @@ typedef struct moe_ws_layout {
   size_t slot_to_union; /* int32  [MOE_MAX_IDS]       slot t = r*k + j -> union index */
   size_t row_mask;      /* uint32 [MOE_MAX_IDS]       bit r: row r chose union expert */
   size_t slot_info;     /* internal per-union-slot weight pointers                    */
+  size_t segments;      /* internal down-sweep work table                             */
   size_t act;           /* bf16   [MOE_MAX_IDS+1][MOE_MAX_ROWS][Imax] silu(g)*u,
                            slot MOE_MAX_IDS = shared expert, Imax = max(I, Is)       */
   size_t y;             /* float  [MOE_MAX_IDS+1][MOE_MAX_ROWS][h] expert outputs     */

@@ -71,7 +71,7 @@ class MoeWeights(ctypes.Structure):
 class MoeWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "sync", "logits", "score", "gamma", "topk_ids", "topk_w", "union_ids", "union_count", "slot_to_union",
-        "row_mask", "slot_info", "act", "y", "total")]
+        "row_mask", "slot_info", "segments", "act", "y", "total")]
 
 
 _lib: Optional[ctypes.CDLL] = None

@@ -52,6 +52,9 @@ struct SweepParams {
   int inter;                  // routed expert intermediate size
   int shared_inter;
   RouteParams route;          // the gate/up sweep takes top-k from route.logits / route.score
+  int32_t* seg_slot;          // [kMaxDownSegs] down segments: union slot
+  uint32_t* seg_rows;         // [kMaxDownSegs] down segments: packed rows and count
+  int32_t* seg_count;         // [1]
 };
 
 constexpr size_t kSlotInfoBytes = 72;  // sizeof(SlotInfo), checked in the kernels file

@@ -335,16 +335,28 @@ __device__ __forceinline__ void stage_rows(u32x4* dst, const uint16_t* src, size
   }
 }
 
-// Copy the slot table (routed slots [0, U) and the shared slot) into LDS.
-// Later reads come from LDS: a global load issued after the prefetched
-// weights would make the in-order load counter drain the prefetch.
-__device__ __forceinline__ void load_slot_table(SlotInfo* dst, const SlotInfo* src, int U) {
+// Copy the slot table into LDS (all 65 entries: those past U are stale and
+// never read, and not waiting for U saves a round trip).  Later reads come
+// from LDS: a global load issued after the prefetched weights would make the
+// in-order load counter drain the prefetch.  Each thread issues all its loads
+// before its first store, so the copy costs one memory round trip, not one
+// per pass of a strided loop.
+template <int kThreads>
+__device__ __forceinline__ void load_slot_table(SlotInfo* dst, const SlotInfo* src) {
   constexpr int kWords = (int)(sizeof(SlotInfo) / 4);
+  constexpr int kPerThread = (kNumSlots * kWords + kThreads - 1) / kThreads;
   const uint32_t* s32 = reinterpret_cast<const uint32_t*>(src);
   uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
-  for (int i = threadIdx.x; i < kNumSlots * kWords; i += blockDim.x) {
-    const int slot = i / kWords;
-    if (slot < U || slot == kSharedSlot) d32[i] = s32[i];
+  uint32_t v[kPerThread];
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int i = (int)threadIdx.x + q * kThreads;
+    v[q] = i < kNumSlots * kWords ? s32[i] : 0u;
+  }
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int i = (int)threadIdx.x + q * kThreads;
+    if (i < kNumSlots * kWords) d32[i] = v[q];
   }
 }
 
@@ -408,6 +420,48 @@ __device__ __forceinline__ SlotInfo slot_info(const RouteParams& rp, int ex, uin
   si.row_mask = row_mask;
   si.expert = ex;
   return si;
+}
+
+// Down-sweep segments (one wave): a segment is one union slot and a group of
+// up to kDownGroup of the rows that use it, routed slots in union order (lane
+// su holds slot su's row mask, 0 past U), then the shared slot's groups of all
+// R rows.  seg_rows[s] holds row i of the group in bits 4i..4i+3 and the row
+// count in bits 28..31.  Returns the number of segments.
+__device__ int build_segments(uint32_t mask, int lane, int R, int32_t* seg_slot, uint32_t* seg_rows) {
+  const int cnt = __popc(mask);
+  const int groups = (cnt + kDownGroup - 1) / kDownGroup;
+  int incl = groups;  // inclusive prefix sum over lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  const int seg = incl - groups;
+  for (int g = 0; g < groups; ++g) {
+    uint32_t packed = 0;
+    int n = 0;
+    for (int r = 0; r < kMaxRows && n < kDownGroup; ++r) {
+      // rows of earlier groups are skipped
+      if (((mask >> r) & 1u) && __popc(mask & ((1u << r) - 1u)) >= g * kDownGroup) {
+        packed |= (uint32_t)r << (4 * n);
+        ++n;
+      }
+    }
+    seg_slot[seg + g] = lane;
+    seg_rows[seg + g] = packed | ((uint32_t)n << 28);
+  }
+  int total = __shfl(incl, 63);
+  for (int g = 0; g * kDownGroup < R; ++g) {
+    uint32_t packed = 0;
+    int n = 0;
+    for (int r = g * kDownGroup; r < R && n < kDownGroup; ++r, ++n) packed |= (uint32_t)r << (4 * n);
+    if (lane == 0) {
+      seg_slot[total] = kSharedSlot;
+      seg_rows[total] = packed | ((uint32_t)n << 28);
+    }
+    ++total;
+  }
+  return total;
 }
 
 // Gate+up sweep.  It starts with the routing decisions: every block runs
@@ -494,6 +548,10 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   }
   __syncthreads();
   const int U = s_union;
+  if (publish && wave == 0) {
+    const int nseg = build_segments(lane < U ? s_slots[lane].row_mask : 0u, lane, R, p.seg_slot, p.seg_rows);
+    if (lane == 0) *p.seg_count = nseg;
+  }
   const long long total = (long long)p.shared_inter + (long long)U * p.inter;
   // Item id of the block's next claim, or -1 once the block's items run out
   // (claims only grow, so every later claim fails too).
@@ -601,6 +659,7 @@ template <int R, int NCH>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   constexpr int kGroup = kDownGroup;  // act rows held per segment (16 VGPRs each per 2048 columns)
   constexpr int kMaxSegs = kMaxDownSegs;
+  (void)R;
   __shared__ SlotInfo s_slots[kNumSlots];
   __shared__ int s_seg_slot[kMaxSegs];
   __shared__ uint32_t s_seg_rows[kMaxSegs];  // row i of the group in bits 4i..4i+3, count in bits 28..31
@@ -609,49 +668,29 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   const int wave = wave_id();
   const int nwaves = blockDim.x >> 6;
   const int h = p.h;
-  const int U = *p.union_count;
-  load_slot_table(s_slots, p.slots, U);
-  __syncthreads();
-  if (wave == 0) {
-    // Segments of routed slot su (lane su < U), in slot order, then the shared slot's.
-    uint32_t mask = lane < U ? s_slots[lane].row_mask : 0u;
-    const int cnt = __popc(mask);
-    const int groups = (cnt + kGroup - 1) / kGroup;
-    int incl = groups;  // inclusive prefix sum over lanes
+  // The slot table and the segment table (written by the gate/up sweep's
+  // block 0), each thread's loads all issued before its first store.
+  {
+    constexpr int kPer = (kMaxSegs + kDownThreads - 1) / kDownThreads;
+    int sl[kPer];
+    uint32_t sr[kPer];
+    const int nseg = *p.seg_count;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
+    for (int q = 0; q < kPer; ++q) {
+      const int i = (int)threadIdx.x + q * kDownThreads;
+      sl[q] = i < kMaxSegs ? p.seg_slot[i] : 0;
+      sr[q] = i < kMaxSegs ? p.seg_rows[i] : 0u;
     }
-    int seg = incl - groups;
-    for (int g = 0; g < groups; ++g) {
-      uint32_t packed = 0;
-      int n = 0;
-      for (int r = 0; r < kMaxRows && n < kGroup; ++r) {
-        if (((mask >> r) & 1u) && n >= 0) {
-          // skip the rows of earlier groups
-          if (__popc(mask & ((1u << r) - 1u)) >= g * kGroup) {
-            packed |= (uint32_t)r << (4 * n);
-            ++n;
-          }
-        }
+    load_slot_table<kDownThreads>(s_slots, p.slots);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int i = (int)threadIdx.x + q * kDownThreads;
+      if (i < kMaxSegs) {
+        s_seg_slot[i] = sl[q];
+        s_seg_rows[i] = sr[q];
       }
-      s_seg_slot[seg + g] = lane;
-      s_seg_rows[seg + g] = packed | ((uint32_t)n << 28);
     }
-    const int nrouted = __shfl(incl, 63);
-    if (lane == 0) {
-      int seg2 = nrouted;
-      for (int g = 0; g * kGroup < R; ++g) {
-        uint32_t packed = 0;
-        int n = 0;
-        for (int r = g * kGroup; r < R && n < kGroup; ++r, ++n) packed |= (uint32_t)r << (4 * n);
-        s_seg_slot[seg2] = kSharedSlot;
-        s_seg_rows[seg2] = packed | ((uint32_t)n << 28);
-        ++seg2;
-      }
-      s_nseg = seg2;
-    }
+    if (threadIdx.x == 0) s_nseg = nseg;
   }
   __syncthreads();
 
