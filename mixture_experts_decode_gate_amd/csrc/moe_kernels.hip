@@ -116,33 +116,53 @@ struct ExpertPtrs {
   float scale2[3];
 };
 
-// Top-k of row r (one wave).  Lane l holds experts l*G .. l*G+G-1, so a lower
-// (lane, position) pair is a lower expert id.  Each of the k rounds takes the
-// lane's largest remaining key (lowest position on ties), the wave-wide
-// maximum of those, and the lowest lane holding it: the largest key, ties to
-// the lower id.  Sigmoid keys are fp32(s) + bias with s the fp64 score the
-// router pass stored.  Writes the row's ids to s_ids; with publish also its
-// ids and weights (fp64, rounded once) to ids_out/w_out.
+// Global-memory load through an address-space-1 pointer: a flat load would
+// also count against the LDS counter, and its wait would drain both.
+template <typename T>
+__device__ __forceinline__ T ld_global(const T* ptr) {
+  typedef __attribute__((address_space(1))) const T global_t;
+  return *(global_t*)ptr;
+}
+
+// The values top-k reads for one row, as lane l sees them (experts
+// l*G .. l*G+G-1, clamped in range).
 template <int G>
-__device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids, bool publish) {
-  const int E = p.E, k = p.k;
-  const bool softmax = p.route_kind == MOE_ROUTE_SOFTMAX;
+struct TopkIn {
   float lv[G], bv[G];
   double sv[G];  // sigmoid score (sigmoid routing)
-  // Every load first (clamped in-bounds indices, no branch) so they overlap.
+};
+
+template <int G>
+__device__ __forceinline__ void topk_load(const RouteParams& p, int r, int lane, TopkIn<G>& in) {
+  const int E = p.E;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const int e = min(lane * G + i, E - 1);
-    lv[i] = p.logits[r * E + e];
-    sv[i] = p.score[r * E + e];
-    bv[i] = p.bias[e];
+    in.lv[i] = ld_global(p.logits + r * E + e);
+    in.sv[i] = ld_global(p.score + r * E + e);
+    in.bv[i] = ld_global(p.bias + e);
   }
+}
+
+// Top-k of row r (one wave) from values loaded by topk_load.  Lane l holds
+// experts l*G .. l*G+G-1, so a lower (lane, position) pair is a lower expert
+// id.  Each of the k rounds takes the lane's largest remaining key (lowest
+// position on ties), the wave-wide maximum of those, and the lowest lane
+// holding it: the largest key, ties to the lower id.  Sigmoid keys are
+// fp32(s) + bias with s the fp64 score the router pass stored.  Writes the
+// row's ids to ids_lds (and ids_out when not null) and, when w_out is not
+// null, the weights (fp64, rounded once).
+template <int G>
+__device__ void topk_select(const RouteParams& p, int r, int lane, TopkIn<G>& in, int32_t* ids_lds,
+                            int32_t* ids_out, float* w_out) {
+  const int E = p.E, k = p.k;
+  const bool softmax = p.route_kind == MOE_ROUTE_SOFTMAX;
   uint32_t key[G];  // 0: not a candidate (past E, or already taken)
   int selj[G];      // round that took the expert, -1 if none
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const bool valid = lane * G + i < E;
-    const float kf = softmax ? lv[i] : (float)sv[i] + bv[i];
+    const float kf = softmax ? in.lv[i] : (float)in.sv[i] + in.bv[i];
     key[i] = valid ? key_bits(kf) : 0u;
     selj[i] = -1;
   }
@@ -173,20 +193,21 @@ __device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids, 
     }
     if (j == 0) top_logit = key_float(m);  // softmax: the largest logit
     if (lane == 0) {
-      if (publish) p.ids_out[r * k + j] = be;
-      s_ids[r * k + j] = be;
+      if (ids_out != nullptr) ids_out[r * k + j] = be;
+      ids_lds[r * k + j] = be;
     }
   }
-  if (!publish) return;
+  if (w_out == nullptr) return;
   // Weights.  Softmax: exp(L - max), normalised over all experts, or over the
   // k selected when norm_topk_prob.  Sigmoid: s, optionally normalised over
   // the selected, times routed_scaling_factor.
-  double all_part = 0.0, sel_part = 0.0;
+  double sv[G], all_part = 0.0, sel_part = 0.0;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
+    sv[i] = 0.0;
     if (lane * G + i < E) {
-      double v = sv[i];
-      if (softmax) v = (!p.norm || selj[i] >= 0) ? exp((double)lv[i] - (double)top_logit) : 0.0;
+      double v = in.sv[i];
+      if (softmax) v = (!p.norm || selj[i] >= 0) ? exp((double)in.lv[i] - (double)top_logit) : 0.0;
       sv[i] = v;
       all_part += v;
       if (selj[i] >= 0) sel_part += v;
@@ -206,7 +227,7 @@ __device__ void topk_row(const RouteParams& p, int r, int lane, int32_t* s_ids, 
         wgt = p.norm ? sv[i] / sel_sum : sv[i];
         wgt *= (double)p.rsf;
       }
-      p.w_out[r * k + selj[i]] = (float)wgt;
+      w_out[r * k + selj[i]] = (float)wgt;
     }
   }
 }
@@ -310,31 +331,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int
   __syncthreads();
   if (!s_last) return;
 
-  if (wave < R) topk_row<G>(p, wave, lane, s_ids, true);
+  if (wave < R) {
+    TopkIn<G> in;
+    topk_load<G>(p, wave, lane, in);
+    topk_select<G>(p, wave, lane, in, s_ids, p.ids_out, p.w_out);
+  }
   // every other block has arrived: reset for the next call
   if (threadIdx.x == 0) __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- sweeps
-// Stage rows of a bf16 [rows][cols] matrix (row stride `stride` elements) into
-// LDS as NCH chunks of 256 swizzled 16-byte units per row, zero beyond
-// `cols`.  Only rows in `mask` are staged.
-template <int R, int NCH>
-__device__ __forceinline__ void stage_rows(u32x4* dst, const uint16_t* src, size_t stride, int cols,
-                                           uint32_t mask) {
-  for (int i = threadIdx.x; i < R * NCH * kChunkUnits; i += blockDim.x) {
-    const int r = i / (NCH * kChunkUnits);
-    if (!((mask >> r) & 1u)) continue;
-    const int rem = i - r * NCH * kChunkUnits;
-    const int c = rem / kChunkUnits;
-    const int un = rem - c * kChunkUnits;
-    const int col = c * kChunk + un * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (col < cols) v = *reinterpret_cast<const u32x4*>(src + (size_t)r * stride + col);
-    dst[(r * NCH + c) * kChunkUnits + swz_unit(un)] = v;
-  }
-}
-
 // Copy the slot table into LDS (all 65 entries: those past U are stale and
 // never read, and not waiting for U saves a round trip).  Later reads come
 // from LDS: a global load issued after the prefetched weights would make the
@@ -372,9 +378,11 @@ struct RowRegs {
 };
 
 // Lanes whose columns lie past K load the row's last 32 columns instead (an
-// in-bounds, finite copy) and zero their two block scales, so they add
-// exactly 0 whatever the activations hold there.  No branch guards the loads
-// (a branch here makes the compiler drain the prefetched loads early).
+// in-bounds, finite copy); scale_pair zeroes their two block scales, so they
+// add exactly 0 whatever the activations hold there.  No branch guards the
+// loads (a branch here makes the compiler drain the prefetched loads early),
+// and nothing is computed on the loaded values until they are used (an
+// operation here would make the compiler wait for them at the fetch).
 template <int NCH>
 __device__ __forceinline__ void load_row(RowRegs<NCH>& b, const uint8_t* packed, const uint8_t* scales, int n,
                                          int K, int lane) {
@@ -383,42 +391,66 @@ __device__ __forceinline__ void load_row(RowRegs<NCH>& b, const uint8_t* packed,
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int col = c * kChunk + lane * 32;
-    const uint32_t keep = col < K ? 0xFFFFu : 0u;
     const int cc = col < K ? col : K - 32;
     b.q[c] = ld_stream(packed + co + (cc >> 1));
-    b.s[c] = ld_stream_u16(scales + so + (cc >> 4)) & keep;
+    b.s[c] = ld_stream_u16(scales + so + (cc >> 4));
   }
 }
 
-// Weight pointers of union slot `slot` for expert ex (ex < 0: the shared
-// expert, used by every row).
-__device__ __forceinline__ SlotInfo slot_info(const RouteParams& rp, int ex, uint32_t row_mask) {
+// The two E4M3 block scales of chunk c for this lane, zero past K.
+template <int NCH>
+__device__ __forceinline__ uint32_t scale_pair(const RowRegs<NCH>& b, int c, int K, int lane) {
+  return c * kChunk + lane * 32 < K ? b.s[c] : 0u;
+}
+
+// Weight pointers of expert ex, as read from the expert tables.
+__device__ __forceinline__ ExpertPtrs expert_ptrs(const RouteParams& rp, int ex) {
+  ExpertPtrs e;
+  e.p[0] = ld_global(rp.gate.packed + ex);
+  e.p[1] = ld_global(rp.gate.scales + ex);
+  e.p[2] = ld_global(rp.up.packed + ex);
+  e.p[3] = ld_global(rp.up.scales + ex);
+  e.p[4] = ld_global(rp.down.packed + ex);
+  e.p[5] = ld_global(rp.down.scales + ex);
+  e.scale2[0] = ld_global(rp.gate.scale2 + ex);
+  e.scale2[1] = ld_global(rp.up.scale2 + ex);
+  e.scale2[2] = ld_global(rp.down.scale2 + ex);
+  return e;
+}
+
+// Slot table entry of a routed expert.
+__device__ __forceinline__ SlotInfo slot_info(const ExpertPtrs& e, int ex, int inter, uint32_t row_mask) {
   SlotInfo si;
-  if (ex >= 0) {
-    si.gate_packed = rp.gate.packed[ex];
-    si.gate_scales = rp.gate.scales[ex];
-    si.up_packed = rp.up.packed[ex];
-    si.up_scales = rp.up.scales[ex];
-    si.down_packed = rp.down.packed[ex];
-    si.down_scales = rp.down.scales[ex];
-    si.gate_scale2 = rp.gate.scale2[ex];
-    si.up_scale2 = rp.up.scale2[ex];
-    si.down_scale2 = rp.down.scale2[ex];
-    si.inter = rp.inter;
-  } else {
-    si.gate_packed = rp.shared_gate.packed;
-    si.gate_scales = rp.shared_gate.scales;
-    si.up_packed = rp.shared_up.packed;
-    si.up_scales = rp.shared_up.scales;
-    si.down_packed = rp.shared_down.packed;
-    si.down_scales = rp.shared_down.scales;
-    si.gate_scale2 = rp.shared_gate.scale2;
-    si.up_scale2 = rp.shared_up.scale2;
-    si.down_scale2 = rp.shared_down.scale2;
-    si.inter = rp.shared_inter;
-  }
+  si.gate_packed = e.p[0];
+  si.gate_scales = e.p[1];
+  si.up_packed = e.p[2];
+  si.up_scales = e.p[3];
+  si.down_packed = e.p[4];
+  si.down_scales = e.p[5];
+  si.gate_scale2 = e.scale2[0];
+  si.up_scale2 = e.scale2[1];
+  si.down_scale2 = e.scale2[2];
+  si.inter = inter;
   si.row_mask = row_mask;
   si.expert = ex;
+  return si;
+}
+
+// Slot table entry of the shared expert (used by every row).
+__device__ __forceinline__ SlotInfo shared_slot_info(const RouteParams& rp, uint32_t row_mask) {
+  SlotInfo si;
+  si.gate_packed = rp.shared_gate.packed;
+  si.gate_scales = rp.shared_gate.scales;
+  si.up_packed = rp.shared_up.packed;
+  si.up_scales = rp.shared_up.scales;
+  si.down_packed = rp.shared_down.packed;
+  si.down_scales = rp.shared_down.scales;
+  si.gate_scale2 = rp.shared_gate.scale2;
+  si.up_scale2 = rp.shared_up.scale2;
+  si.down_scale2 = rp.shared_down.scale2;
+  si.inter = rp.shared_inter;
+  si.row_mask = row_mask;
+  si.expert = -1;
   return si;
 }
 
@@ -484,9 +516,16 @@ __device__ int build_segments(uint32_t mask, int lane, int R, int32_t* seg_slot,
 //   act[slot][r][n] = bf16(silu(g) * v), g = W_gate[n,:] . x_r, v = W_up[n,:] . x_r.
 template <int R, int NCH, int G>
 __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p) {
+  constexpr int kXUnits = R * NCH * kChunkUnits;  // 16-byte units of staged x
+  constexpr int kXPer = (kXUnits + kMaxSweepThreads - 1) / kMaxSweepThreads;
+  constexpr bool kPtab = G == 4;  // E <= 256: every expert's pointers fit in LDS
   extern __shared__ u32x4 xs[];  // [R][NCH][256] staged x rows
   __shared__ SlotInfo s_slots[kNumSlots];
+  __shared__ ExpertPtrs s_ptab[kPtab ? 64 * G : 1];
   __shared__ __align__(16) int32_t s_ids[kMaxIds];
+  __shared__ float s_w[kMaxIds];
+  __shared__ int32_t s_uids[kMaxIds], s_s2u[kMaxIds];
+  __shared__ uint32_t s_rmask[kMaxIds];
   __shared__ int s_next;  // the block's next unclaimed item
   __shared__ int s_union;
   const int lane = threadIdx.x & 63;
@@ -494,11 +533,37 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   const int h = p.h;
   const RouteParams& rp = p.route;
   const bool publish = blockIdx.x == 0;
+
+  // Prologue.  Every load that does not depend on routing is issued first --
+  // x, the top-k inputs, every expert's weight pointers, then the first
+  // item's weights -- and each is consumed in issue order, so no wait on the
+  // in-order load counter covers a load issued after it.  No global store
+  // precedes a barrier (a barrier after a store waits for every outstanding
+  // load): block 0 writes the routing results to the workspace only after
+  // the last barrier.
+  u32x4 xv[kXPer];
+  auto x_unit = [&](int i, int& r, int& dst) {  // unit i of the staged x: its row, LDS slot and column
+    r = i / (NCH * kChunkUnits);
+    const int rem = i - r * NCH * kChunkUnits;
+    const int c = rem / kChunkUnits, un = rem - c * kChunkUnits;
+    dst = (r * NCH + c) * kChunkUnits + swz_unit(un);
+    return c * kChunk + un * 8;
+  };
+#pragma unroll
+  for (int q = 0; q < kXPer; ++q) {
+    int r, dst;
+    const int col = x_unit(min((int)threadIdx.x + q * kMaxSweepThreads, kXUnits - 1), r, dst);
+    xv[q] = ld_global(reinterpret_cast<const u32x4*>(p.x + (size_t)r * h + (col < h ? col : h - 8)));
+  }
+  // Unconditional, with clamped indices: a branch around a load would leave
+  // the wait-count pass unsure of the count and make it wait for everything.
+  TopkIn<G> tin;
+  topk_load<G>(rp, wave < R ? wave : R - 1, lane, tin);
+  ExpertPtrs ep;
+  if (kPtab) ep = expert_ptrs(rp, min((int)threadIdx.x, rp.E - 1));
   if (threadIdx.x == 0) {
     s_next = 0;
-    const SlotInfo si = slot_info(rp, -1, (1u << R) - 1u);
-    s_slots[kSharedSlot] = si;
-    if (publish) rp.slots[kSharedSlot] = si;
+    s_slots[kSharedSlot] = shared_slot_info(rp, (1u << R) - 1u);
   }
   __syncthreads();
 
@@ -527,31 +592,39 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     load_row<NCH>(u, si.up_packed, si.up_scales, n, h, lane);
   };
   // A first claim on a shared-expert row needs no routing: its weights are
-  // requested now and arrive while the block runs top-k.
+  // requested now and arrive while the block runs top-k.  A wave whose first
+  // claim is a routed row loads a shared row some other wave claimed (a cache
+  // hit) so the load stays unconditional, and fetches its item later.
   long long first = claim_id();
   const bool early = first < p.shared_inter;
-  if (early) fetch((int)first, ga, ua, sa, na, slot_a);
+  fetch(early ? (int)first : (int)(first % p.shared_inter), ga, ua, sa, na, slot_a);
+  // Nothing that reads a loaded value may be scheduled above the fetch.
+  __builtin_amdgcn_sched_barrier(0);
 
-  if (wave < R) topk_row<G>(rp, wave, lane, s_ids, publish);
+  // Consume, in issue order: x (zero past h), top-k, the pointer table.
+#pragma unroll
+  for (int q = 0; q < kXPer; ++q) {
+    const int i = (int)threadIdx.x + q * kMaxSweepThreads;
+    if (i < kXUnits) {
+      int r, dst;
+      const int col = x_unit(i, r, dst);
+      xs[dst] = col < h ? xv[q] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  if (wave < R) topk_select<G>(rp, wave, lane, tin, s_ids, nullptr, publish ? s_w : nullptr);
+  if (kPtab && (int)threadIdx.x < rp.E) s_ptab[threadIdx.x] = ep;
   __syncthreads();
   if (wave == 0) {
     uint32_t mask;
     int count;
-    const int pos = union_wave(s_ids, R * rp.k, rp.k, R, lane, publish ? rp.union_ids : nullptr, rp.union_count,
-                               rp.slot_to_union, rp.row_mask, &mask, &count);
+    const int pos = union_wave(s_ids, R * rp.k, rp.k, R, lane, s_uids, &s_union, s_s2u, s_rmask, &mask, &count);
     if (pos >= 0) {  // lane is the union entry's first slot
-      const SlotInfo si = slot_info(rp, s_ids[lane], mask);
-      s_slots[pos] = si;
-      if (publish) rp.slots[pos] = si;
+      const int ex = s_ids[lane];
+      s_slots[pos] = slot_info(kPtab ? s_ptab[ex] : expert_ptrs(rp, ex), ex, rp.inter, mask);
     }
-    if (lane == 0) s_union = count;
   }
   __syncthreads();
   const int U = s_union;
-  if (publish && wave == 0) {
-    const int nseg = build_segments(lane < U ? s_slots[lane].row_mask : 0u, lane, R, p.seg_slot, p.seg_rows);
-    if (lane == 0) *p.seg_count = nseg;
-  }
   const long long total = (long long)p.shared_inter + (long long)U * p.inter;
   // Item id of the block's next claim, or -1 once the block's items run out
   // (claims only grow, so every later claim fails too).
@@ -574,8 +647,9 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
       bf16x2 gw[16], uw[16];
       decode32(g.q[c], gw);
       decode32(u.q[c], uw);
-      const float gs0 = e4m3<0>(g.s[c]), gs1 = e4m3<1>(g.s[c]);
-      const float us0 = e4m3<0>(u.s[c]), us1 = e4m3<1>(u.s[c]);
+      const uint32_t gsc = scale_pair<NCH>(g, c, h, lane), usc = scale_pair<NCH>(u, c, h, lane);
+      const float gs0 = e4m3<0>(gsc), gs1 = e4m3<1>(gsc);
+      const float us0 = e4m3<0>(usc), us1 = e4m3<1>(usc);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         if ((si.row_mask >> r) & 1u) {
@@ -604,9 +678,7 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   // Three register buffers in rotation: while one item is computed, the next
   // two are in flight.  Loads are always issued (a valid item repeated once
   // the claims run out) so no branch separates them from the compute they
-  // overlap.  The first two items' weights are requested before x is staged,
-  // so their latency overlaps the staging; waves without work still stage and
-  // sync.
+  // overlap.
   RowRegs<NCH> gc, uc;
   SlotInfo sc;
   int nc = 0, slot_c = 0;
@@ -617,8 +689,26 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     if (!early) fetch(id_a, ga, ua, sa, na, slot_a);
     fetch(id_b >= 0 ? id_b : id_a, gb, ub, sb, nb, slot_b);
   }
-  stage_rows<R, NCH>(xs, p.x, (size_t)h, h, (1u << R) - 1u);
-  __syncthreads();
+  // Block 0 publishes the routing results for the down sweep and the blend.
+  if (publish && wave == 0) {
+    const int n = R * rp.k;
+    if (lane < n) {
+      rp.ids_out[lane] = s_ids[lane];
+      rp.w_out[lane] = s_w[lane];
+      rp.slot_to_union[lane] = s_s2u[lane];
+    }
+    if (lane < U) {
+      rp.union_ids[lane] = s_uids[lane];
+      rp.row_mask[lane] = s_rmask[lane];
+      rp.slots[lane] = s_slots[lane];
+    }
+    if (lane == 0) {
+      *rp.union_count = U;
+      rp.slots[kSharedSlot] = s_slots[kSharedSlot];
+    }
+    const int nseg = build_segments(lane < U ? s_slots[lane].row_mask : 0u, lane, R, p.seg_slot, p.seg_rows);
+    if (lane == 0) *p.seg_count = nseg;
+  }
   if (!has_work) return;
   while (true) {
     const int id_c = id_b >= 0 ? claim() : -1;
@@ -754,7 +844,8 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
         for (int c = 0; c < NCH; ++c) {
           bf16x2 dw[16];
           decode32(b.row[i].q[c], dw);
-          const float s0 = e4m3<0>(b.row[i].s[c]), s1 = e4m3<1>(b.row[i].s[c]);
+          const uint32_t sc = scale_pair<NCH>(b.row[i], c, K, lane);
+          const float s0 = e4m3<0>(sc), s1 = e4m3<1>(sc);
 #pragma unroll
           for (int g = 0; g < kGroup; ++g)
             if (g < cnt)
@@ -850,8 +941,7 @@ int env_int(const char* name, int dflt) {
 
 // Sweep launch shape: threads per block and blocks per CU.  Blocks per CU is
 // the occupancy limit (queried once per kernel instance) capped so a CU runs
-// about kWavesPerCu waves; MOE_SWEEP_THREADS and MOE_WAVES_PER_CU override the
-// defaults for tuning runs.
+// about 8 waves; MOE_WAVES_PER_CU overrides that for tuning runs.
 struct SweepShape {
   int threads = 0;
   int per_cu = 0;
@@ -860,8 +950,7 @@ struct SweepShape {
 template <typename K>
 dim3 sweep_grid(K kernel, size_t lds, int max_blocks, SweepShape& cache, int default_threads) {
   if (cache.threads <= 0) {
-    int threads = env_int("MOE_SWEEP_THREADS", default_threads);
-    if (threads > kMaxSweepThreads || threads % 64) threads = default_threads;
+    const int threads = default_threads;
     const int waves_per_cu = env_int("MOE_WAVES_PER_CU", 8);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu <= 0)
@@ -896,7 +985,7 @@ hipError_t gateup_rng(const SweepParams& p, int max_items, hipStream_t s) {
     attr_set = true;
   }
   static SweepShape shape;
-  const dim3 grid = sweep_grid(gateup_kernel<R, NCH, G>, lds, 1 << 30, shape, 512);
+  const dim3 grid = sweep_grid(gateup_kernel<R, NCH, G>, lds, 1 << 30, shape, kMaxSweepThreads);
   const int waves = (int)grid.x * (shape.threads / 64);
   dim3 g = grid;
   if (waves > max_items) g.x = (max_items * 64 + shape.threads - 1) / shape.threads;
