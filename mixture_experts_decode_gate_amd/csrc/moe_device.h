@@ -85,9 +85,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // wave_sum of N independent values, step by step, so each DPP step of one
 // value fills the hazard slots of the others.  Same addition order as
-// wave_sum for every value.
+// wave_sum for every value.  The totals are valid in lane 63 only.
 template <int N>
-__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+__device__ __forceinline__ void wave_sum_lane63_n(float (&v)[N]) {
 #define MOE_SUM_STEP(CTRL, MASK)                                                                   \
   _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] += __builtin_bit_cast(                        \
       float, dpp_u32<CTRL, MASK>(__builtin_bit_cast(uint32_t, v[i])));
@@ -98,6 +98,12 @@ __device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
   MOE_SUM_STEP(0x142, 0xA)
   MOE_SUM_STEP(0x143, 0xC)
 #undef MOE_SUM_STEP
+}
+
+// The same, with the totals broadcast to every lane.
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+  wave_sum_lane63_n<N>(v);
 #pragma unroll
   for (int i = 0; i < N; ++i) v[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[i]), 63));
 }
@@ -160,6 +166,19 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 
 // The wave's index within its block, as a scalar (wave-uniform) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// A wave-uniform value read from LDS, moved to scalar registers, so the
+// address arithmetic built on it runs on the scalar unit.
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint64_t lo = uniform_u32((uint32_t)v), hi = uniform_u32((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>((hi << 32) | lo);
+}
 
 typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
 typedef __attribute__((address_space(1))) const uint16_t global_u16;

@@ -383,18 +383,32 @@ struct RowRegs {
 // loads (a branch here makes the compiler drain the prefetched loads early),
 // and nothing is computed on the loaded values until they are used (an
 // operation here would make the compiler wait for them at the fetch).
+// packed, scales, n and K are wave-uniform (scalar registers): each load is
+// a scalar row base plus the lane's unsigned 32-bit offset, with no vector
+// address arithmetic.
 template <int NCH>
 __device__ __forceinline__ void load_row(RowRegs<NCH>& b, const uint8_t* packed, const uint8_t* scales, int n,
                                          int K, int lane) {
-  const size_t co = (size_t)n * (size_t)(K >> 1);
-  const size_t so = (size_t)n * (size_t)(K >> 4);
+  const uint8_t* rc = packed + (size_t)n * (size_t)(K >> 1);
+  const uint8_t* rs = scales + (size_t)n * (size_t)(K >> 4);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int col = c * kChunk + lane * 32;
-    const int cc = col < K ? col : K - 32;
-    b.q[c] = ld_stream(packed + co + (cc >> 1));
-    b.s[c] = ld_stream_u16(scales + so + (cc >> 4));
+    const uint32_t cc = (uint32_t)(col < K ? col : K - 32);
+    b.q[c] = ld_stream(rc + (cc >> 1));
+    b.s[c] = ld_stream_u16(rs + (cc >> 4));
   }
+}
+
+// Reads the row's loaded registers here, on every path.  Where a path skips
+// the use of a prefetched row (a branch on the rows that use it, an item that
+// is not computed), the compiler's wait-count pass counts the row's loads as
+// still in flight after it, and the next write to those registers (at the
+// top of the loop) waits for every load issued since.
+template <int NCH>
+__device__ __forceinline__ void consume(const RowRegs<NCH>& b) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) asm volatile("" ::"v"(b.q[c]), "v"(b.s[c]));
 }
 
 // The two E4M3 block scales of chunk c for this lane, zero past K.
@@ -576,10 +590,15 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     i = __builtin_amdgcn_readfirstlane(i);
     return (long long)blockIdx.x + (long long)i * gridDim.x;
   };
+  // What the compute needs of an item's slot, in scalar registers.
+  struct ItemSlot {
+    uint32_t row_mask;
+    float gate_scale2, up_scale2;
+  };
   RowRegs<NCH> ga, ua, gb, ub;
-  SlotInfo sa, sb;
+  ItemSlot sa, sb;
   int na = 0, nb = 0, slot_a = 0, slot_b = 0;
-  auto fetch = [&](int id, RowRegs<NCH>& g, RowRegs<NCH>& u, SlotInfo& si, int& n, int& slot) {
+  auto fetch = [&](int id, RowRegs<NCH>& g, RowRegs<NCH>& u, ItemSlot& si, int& n, int& slot) {
     if (id < p.shared_inter) {
       slot = kSharedSlot;
       n = id;
@@ -587,17 +606,23 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
       slot = (id - p.shared_inter) / p.inter;
       n = id - p.shared_inter - slot * p.inter;
     }
-    si = s_slots[slot];
-    load_row<NCH>(g, si.gate_packed, si.gate_scales, n, h, lane);
-    load_row<NCH>(u, si.up_packed, si.up_scales, n, h, lane);
+    const SlotInfo& e = s_slots[slot];
+    load_row<NCH>(g, uniform_ptr(e.gate_packed), uniform_ptr(e.gate_scales), n, h, lane);
+    load_row<NCH>(u, uniform_ptr(e.up_packed), uniform_ptr(e.up_scales), n, h, lane);
+    si.row_mask = uniform_u32(e.row_mask);
+    si.gate_scale2 = uniform_f32(e.gate_scale2);
+    si.up_scale2 = uniform_f32(e.up_scale2);
   };
   // A first claim on a shared-expert row needs no routing: its weights are
   // requested now and arrive while the block runs top-k.  A wave whose first
   // claim is a routed row loads a shared row some other wave claimed (a cache
-  // hit) so the load stays unconditional, and fetches its item later.
+  // hit; it is not computed) so the load stays unconditional, and fetches its
+  // item later.  That shared row also stands in for every item past the last
+  // claim: its loads are always in bounds.
   long long first = claim_id();
   const bool early = first < p.shared_inter;
-  fetch(early ? (int)first : (int)(first % p.shared_inter), ga, ua, sa, na, slot_a);
+  const int any_id = early ? (int)first : (int)(first % p.shared_inter);
+  fetch(any_id, ga, ua, sa, na, slot_a);
   // Nothing that reads a loaded value may be scheduled above the fetch.
   __builtin_amdgcn_sched_barrier(0);
 
@@ -610,6 +635,18 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
       const int col = x_unit(i, r, dst);
       xs[dst] = col < h ? xv[q] : u32x4{0u, 0u, 0u, 0u};
     }
+  }
+  // Every prologue load is waited for here on every path (see consume()),
+  // used or not.
+#pragma unroll
+  for (int q = 0; q < kXPer; ++q) asm volatile("" ::"v"(xv[q]));
+#pragma unroll
+  for (int i = 0; i < G; ++i) asm volatile("" ::"v"(tin.lv[i]), "v"(tin.bv[i]), "v"(tin.sv[i]));
+  if (kPtab) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) asm volatile("" ::"v"(ep.p[i]));
+#pragma unroll
+    for (int i = 0; i < 3; ++i) asm volatile("" ::"v"(ep.scale2[i]));
   }
   if (wave < R) topk_select<G>(rp, wave, lane, tin, s_ids, nullptr, publish ? s_w : nullptr);
   if (kPtab && (int)threadIdx.x < rp.E) s_ptab[threadIdx.x] = ep;
@@ -633,7 +670,7 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     return id < total ? (int)id : -1;
   };
 
-  auto compute = [&](const RowRegs<NCH>& g, const RowRegs<NCH>& u, const SlotInfo& si, int n, int slot) {
+  auto compute = [&](const RowRegs<NCH>& g, const RowRegs<NCH>& u, const ItemSlot& si, int n, int slot) {
     float ag[R], au[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -676,19 +713,24 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   };
 
   // Three register buffers in rotation: while one item is computed, the next
-  // two are in flight.  Loads are always issued (a valid item repeated once
-  // the claims run out) so no branch separates them from the compute they
-  // overlap.
+  // two are in flight.  Loads are always issued (the stand-in row once the
+  // claims run out) so no branch separates them from the compute they
+  // overlap.  An item id of -1 is loaded and waited for but not computed:
+  // the first buffer of a wave whose first claim is a routed row, and every
+  // buffer past the last claim.
   RowRegs<NCH> gc, uc;
-  SlotInfo sc;
+  ItemSlot sc;
   int nc = 0, slot_c = 0;
-  int id_a = first < total ? (int)first : -1;
-  const bool has_work = id_a >= 0;
-  int id_b = has_work ? claim() : -1;
-  if (has_work) {
-    if (!early) fetch(id_a, ga, ua, sa, na, slot_a);
-    fetch(id_b >= 0 ? id_b : id_a, gb, ub, sb, nb, slot_b);
+  int id_a, id_b;
+  if (early) {
+    id_a = (int)first;  // first < Is <= total
+    id_b = claim();
+  } else {
+    id_a = -1;
+    id_b = first < total ? (int)first : -1;
   }
+  const bool has_work = id_a >= 0 || id_b >= 0;
+  fetch(id_b >= 0 ? id_b : any_id, gb, ub, sb, nb, slot_b);
   // Block 0 publishes the routing results for the down sweep and the blend.
   if (publish && wave == 0) {
     const int n = R * rp.k;
@@ -710,18 +752,27 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     if (lane == 0) *p.seg_count = nseg;
   }
   if (!has_work) return;
+  // One exit, after a whole rotation: an exit after each item would give the
+  // compiler paths back to the top with items still in flight, and the waits
+  // it derives for those paths would drain the loads on every pass.  Items
+  // past the last claim are waited for (their loads repeat a valid item) but
+  // not computed.
   while (true) {
     const int id_c = id_b >= 0 ? claim() : -1;
-    fetch(id_c >= 0 ? id_c : id_a, gc, uc, sc, nc, slot_c);
-    compute(ga, ua, sa, na, slot_a);
-    if (id_b < 0) break;
+    fetch(id_c >= 0 ? id_c : any_id, gc, uc, sc, nc, slot_c);
+    consume<NCH>(ga);
+    consume<NCH>(ua);
+    if (id_a >= 0) compute(ga, ua, sa, na, slot_a);
     const int id_a2 = id_c >= 0 ? claim() : -1;
-    fetch(id_a2 >= 0 ? id_a2 : id_b, ga, ua, sa, na, slot_a);
-    compute(gb, ub, sb, nb, slot_b);
-    if (id_c < 0) break;
+    fetch(id_a2 >= 0 ? id_a2 : any_id, ga, ua, sa, na, slot_a);
+    consume<NCH>(gb);
+    consume<NCH>(ub);
+    if (id_b >= 0) compute(gb, ub, sb, nb, slot_b);
     const int id_b2 = id_a2 >= 0 ? claim() : -1;
-    fetch(id_b2 >= 0 ? id_b2 : id_c, gb, ub, sb, nb, slot_b);
-    compute(gc, uc, sc, nc, slot_c);
+    fetch(id_b2 >= 0 ? id_b2 : any_id, gb, ub, sb, nb, slot_b);
+    consume<NCH>(gc);
+    consume<NCH>(uc);
+    if (id_c >= 0) compute(gc, uc, sc, nc, slot_c);
     if (id_a2 < 0) break;
     id_a = id_a2;
     id_b = id_b2;
@@ -800,11 +851,14 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
     const int first = (int)(((long long)V * seg + nseg - 1) / nseg);  // first virtual wave of the segment
     const int last = (int)(((long long)V * (seg + 1) + nseg - 1) / nseg);
     const int n_end = h;
-    const int slot = s_seg_slot[seg];
-    const uint32_t rows = s_seg_rows[seg];
+    const int slot = uniform_int(s_seg_slot[seg]);
+    const uint32_t rows = uniform_u32(s_seg_rows[seg]);
     const int cnt = (int)(rows >> 28);
     const SlotInfo& si = s_slots[slot];
-    const int K = si.inter;
+    const int K = uniform_int(si.inter);
+    const uint8_t* const d_packed = uniform_ptr(si.down_packed);
+    const uint8_t* const d_scales = uniform_ptr(si.down_scales);
+    const float d2 = uniform_f32(si.down_scale2);
     const int stride = (last - first) * kDownBatch;
     const int n0 = (v - first) * kDownBatch;
     if (n0 >= n_end) continue;
@@ -826,7 +880,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
 #pragma unroll
       for (int i = 0; i < kDownBatch; ++i) {
         const int n = nb + i < n_end ? nb + i : n_end - 1;  // rows past the range are loaded, not computed
-        load_row<NCH>(b.row[i], si.down_packed, si.down_scales, n, K, lane);
+        load_row<NCH>(b.row[i], d_packed, d_scales, n, K, lane);
       }
     };
     // Rows of a batch: per group row, the batch's dot products are reduced
@@ -859,7 +913,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
           const int r = (int)((rows >> (4 * g)) & 0xFu);
           float* dst = p.y + ((size_t)slot * kMaxRows + r) * h + nb;
           if (lane == 0) {
-            const float d2 = si.down_scale2;
+
 #pragma unroll
             for (int i = 0; i < kDownBatch; i += 4) {
               if (nb + i + 4 <= n_end) {
@@ -877,23 +931,36 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
     };
     // kDownBufs batches in rotation: while one is computed, the next
     // kDownBufs - 1 are in flight.  Batches past the range reload the last
-    // row (no branch around the loads) and are not computed.
+    // row (no branch around the loads); they are waited for but not
+    // computed.  The loop runs whole rotations with one way back to the top:
+    // an exit after each batch would give the compiler paths back to the top
+    // with batches still in flight, and the waits it derives for those paths
+    // would drain the loads on every pass.
     int nf = n0;  // next batch to fetch
 #pragma unroll
     for (int i = 0; i < kDownBufs - 1; ++i) {
       fetch(nf < n_end ? nf : n_end - 1, buf[i]);
       nf += stride;
     }
-    for (int nc = n0;;) {
+    // The act rows are waited for here, on every path (see consume()).
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) asm volatile("" ::"v"(act[i][c][u]));
+    const int rounds = ((n_end - n0 + stride - 1) / stride + kDownBufs - 1) / kDownBufs;
+    int nc = n0;
+    for (int it = 0; it < rounds; ++it) {
 #pragma unroll
       for (int i = 0; i < kDownBufs; ++i) {
         fetch(nf < n_end ? nf : n_end - 1, buf[(i + kDownBufs - 1) % kDownBufs]);
         nf += stride;
-        compute(nc, buf[i]);
+#pragma unroll
+        for (int q = 0; q < kDownBatch; ++q) consume<NCH>(buf[i].row[q]);
+        if (nc < n_end) compute(nc, buf[i]);
         nc += stride;
-        if (nc >= n_end) break;
       }
-      if (nc >= n_end) break;
     }
   }
 }
