@@ -144,7 +144,8 @@ void compute_layout(const moe_config* c, moe_ws_layout* L) {
   L->slot_to_union = take(MOE_MAX_IDS * sizeof(int32_t));
   L->row_mask = take(MOE_MAX_IDS * sizeof(uint32_t));
   L->slot_info = take((MOE_MAX_IDS + 1) * moe::kSlotInfoBytes);
-  L->segments = take(sizeof(int32_t) + (size_t)moe::kMaxDownSegs * (sizeof(int32_t) + sizeof(uint32_t)));
+  L->segments = take(sizeof(int32_t) + (size_t)moe::kMaxDownSegs * (sizeof(int32_t) + sizeof(uint32_t)) +
+                     (size_t)(moe::kMaxDownSegs + 1) * sizeof(int32_t));
   L->act = take((MOE_MAX_IDS + 1) * R * imax * sizeof(uint16_t));
   L->y = take((MOE_MAX_IDS + 1) * R * h * sizeof(float));
   L->total = off;
@@ -252,6 +253,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
   sp.seg_count = reinterpret_cast<int32_t*>(wsb + L.segments);
   sp.seg_slot = sp.seg_count + 1;
   sp.seg_rows = reinterpret_cast<uint32_t*>(sp.seg_slot + moe::kMaxDownSegs);
+  sp.seg_cum = reinterpret_cast<int32_t*>(sp.seg_rows + moe::kMaxDownSegs);
 
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return device_status(e, "event record");

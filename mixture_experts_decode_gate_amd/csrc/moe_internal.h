@@ -15,6 +15,9 @@ struct SlotInfo;
 constexpr size_t kSyncBytes = 256;
 constexpr int kDownGroup = 2;  // act rows a down segment carries
 constexpr int kMaxDownSegs = (MOE_MAX_IDS + 1) * ((MOE_MAX_ROWS + kDownGroup - 1) / kDownGroup);
+// Down-sweep work weight of a segment with n rows: kSegCostBase + n per
+// weight row (decode and loads, plus one dot product per row).
+constexpr int kSegCostBase = 3;
 
 struct RouteParams {
   const uint16_t* x;       // [rows][h] bf16
@@ -54,6 +57,7 @@ struct SweepParams {
   RouteParams route;          // the gate/up sweep takes top-k from route.logits / route.score
   int32_t* seg_slot;          // [kMaxDownSegs] down segments: union slot
   uint32_t* seg_rows;         // [kMaxDownSegs] down segments: packed rows and count
+  int32_t* seg_cum;           // [kMaxDownSegs + 1] down segments: weight before segment s
   int32_t* seg_count;         // [1]
 };
 

@@ -38,10 +38,10 @@ namespace moe {
 // the arrival counter; the block that draws the last ticket reads every logit
 // and runs top-k (one wave per row), then resets the counter to zero for the
 // next call.
-constexpr int kRouterChunk = 1024;
+constexpr int kRouterChunk = 512;
 constexpr int kMaxRouterChunks = MOE_MAX_DIM / kRouterChunk;
-constexpr int kRouteThreads = 64 * kMaxRows;  // >= one wave per row for top-k, >= nkc waves
-static_assert(kMaxRouterChunks <= kMaxRows, "route blocks need a wave per router chunk");
+// A wave per router chunk, and at least one per row for top-k.
+constexpr int kRouteThreads = 64 * (kMaxRouterChunks > kMaxRows ? kMaxRouterChunks : kMaxRows);
 static_assert(MOE_MAX_EXPERTS <= 64 * 16, "top-k holds at most 16 keys per lane");
 
 // Union of the n <= 64 ids in ids_lds (slot t = r*k + j).  Lane t compares its
@@ -472,17 +472,24 @@ __device__ __forceinline__ SlotInfo shared_slot_info(const RouteParams& rp, uint
 // up to kDownGroup of the rows that use it, routed slots in union order (lane
 // su holds slot su's row mask, 0 past U), then the shared slot's groups of all
 // R rows.  seg_rows[s] holds row i of the group in bits 4i..4i+3 and the row
-// count in bits 28..31.  Returns the number of segments.
-__device__ int build_segments(uint32_t mask, int lane, int R, int32_t* seg_slot, uint32_t* seg_rows) {
+// count in bits 28..31; seg_cum[s] is the summed work weight of the segments
+// before s (seg_cum[count] the total).  Returns the number of segments.
+__device__ int build_segments(uint32_t mask, int lane, int R, int32_t* seg_slot, uint32_t* seg_rows,
+                              int32_t* seg_cum) {
   const int cnt = __popc(mask);
   const int groups = (cnt + kDownGroup - 1) / kDownGroup;
-  int incl = groups;  // inclusive prefix sum over lanes
+  int incl = groups;                          // inclusive prefix sums over lanes: segments
+  int wincl = groups * kSegCostBase + cnt;    // and weight
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
+    const int v = __shfl_up(incl, o), wv = __shfl_up(wincl, o);
+    if (lane >= o) {
+      incl += v;
+      wincl += wv;
+    }
   }
   const int seg = incl - groups;
+  int wcum = wincl - (groups * kSegCostBase + cnt);
   for (int g = 0; g < groups; ++g) {
     uint32_t packed = 0;
     int n = 0;
@@ -495,8 +502,11 @@ __device__ int build_segments(uint32_t mask, int lane, int R, int32_t* seg_slot,
     }
     seg_slot[seg + g] = lane;
     seg_rows[seg + g] = packed | ((uint32_t)n << 28);
+    seg_cum[seg + g] = wcum;
+    wcum += kSegCostBase + n;
   }
   int total = __shfl(incl, 63);
+  wcum = __shfl(wincl, 63);
   for (int g = 0; g * kDownGroup < R; ++g) {
     uint32_t packed = 0;
     int n = 0;
@@ -504,9 +514,12 @@ __device__ int build_segments(uint32_t mask, int lane, int R, int32_t* seg_slot,
     if (lane == 0) {
       seg_slot[total] = kSharedSlot;
       seg_rows[total] = packed | ((uint32_t)n << 28);
+      seg_cum[total] = wcum;
     }
+    wcum += kSegCostBase + n;
     ++total;
   }
+  if (lane == 0) seg_cum[total] = wcum;
   return total;
 }
 
@@ -748,7 +761,8 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
       *rp.union_count = U;
       rp.slots[kSharedSlot] = s_slots[kSharedSlot];
     }
-    const int nseg = build_segments(lane < U ? s_slots[lane].row_mask : 0u, lane, R, p.seg_slot, p.seg_rows);
+    const int nseg =
+        build_segments(lane < U ? s_slots[lane].row_mask : 0u, lane, R, p.seg_slot, p.seg_rows, p.seg_cum);
     if (lane == 0) *p.seg_count = nseg;
   }
   if (!has_work) return;
@@ -804,6 +818,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   __shared__ SlotInfo s_slots[kNumSlots];
   __shared__ int s_seg_slot[kMaxSegs];
   __shared__ uint32_t s_seg_rows[kMaxSegs];  // row i of the group in bits 4i..4i+3, count in bits 28..31
+  __shared__ int s_seg_cum[kMaxSegs + 1];    // work weight before segment s
   __shared__ int s_nseg;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -812,15 +827,17 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   // The slot table and the segment table (written by the gate/up sweep's
   // block 0), each thread's loads all issued before its first store.
   {
-    constexpr int kPer = (kMaxSegs + kDownThreads - 1) / kDownThreads;
-    int sl[kPer];
+    constexpr int kPer = (kMaxSegs + 1 + kDownThreads - 1) / kDownThreads;
+    int sl[kPer], sw[kPer];
     uint32_t sr[kPer];
     const int nseg = *p.seg_count;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const int i = (int)threadIdx.x + q * kDownThreads;
-      sl[q] = i < kMaxSegs ? p.seg_slot[i] : 0;
-      sr[q] = i < kMaxSegs ? p.seg_rows[i] : 0u;
+      const int ic = i < kMaxSegs ? i : kMaxSegs - 1;
+      sl[q] = p.seg_slot[ic];
+      sr[q] = p.seg_rows[ic];
+      sw[q] = p.seg_cum[i <= kMaxSegs ? i : kMaxSegs];
     }
     load_slot_table<kDownThreads>(s_slots, p.slots);
 #pragma unroll
@@ -830,26 +847,36 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
         s_seg_slot[i] = sl[q];
         s_seg_rows[i] = sr[q];
       }
+      if (i <= kMaxSegs) s_seg_cum[i] = sw[q];
     }
     if (threadIdx.x == 0) s_nseg = nseg;
   }
   __syncthreads();
 
-  // Each segment gets a group of waves in proportion (virtual wave v of V
-  // works on segment v * nseg / V), and the group's waves take interleaved
-  // batches of kDownBatch rows: every group sweeps its matrix front to back
-  // together.  With fewer waves than segments a wave takes several virtual
-  // waves in turn.
+  // Each segment gets a group of waves in proportion to its work weight
+  // (kSegCostBase + rows per weight row: a two-row segment costs more
+  // arithmetic per byte): with cumulative weights c_s and total C, virtual
+  // wave v of V works on the segment s with c_s <= v * C / V < c_{s+1}.  The
+  // group's waves take interleaved batches of kDownBatch rows: every group
+  // sweeps its matrix front to back together.  V >= C gives every segment
+  // at least one virtual wave; with fewer waves than that a wave takes
+  // several virtual waves in turn.
   const int W = gridDim.x * nwaves;
   const int nseg = s_nseg;
-  const int V = W > nseg ? W : nseg;
+  const int C = s_seg_cum[nseg];
+  const int V = W > C ? W : C;
 
   DownBatch<NCH> buf[kDownBufs];
   u32x4 act[kGroup][NCH][4];
   for (int v = blockIdx.x * nwaves + wave; v < V; v += W) {
-    const int seg = (int)((long long)v * nseg / V);
-    const int first = (int)(((long long)V * seg + nseg - 1) / nseg);  // first virtual wave of the segment
-    const int last = (int)(((long long)V * (seg + 1) + nseg - 1) / nseg);
+    const long long key = (long long)v * C / V;  // in [0, C)
+    int seg = 0;
+    for (int span = 64; span > 0; span >>= 1)  // largest s with c_s <= key (nseg <= 128)
+      if (seg + span < nseg && s_seg_cum[seg + span] <= key) seg += span;
+    seg = uniform_int(seg);
+    const long long c0 = s_seg_cum[seg], c1 = s_seg_cum[seg + 1];
+    const int first = (int)(((long long)V * c0 + C - 1) / C);  // first virtual wave of the segment
+    const int last = (int)(((long long)V * c1 + C - 1) / C);
     const int n_end = h;
     const int slot = uniform_int(s_seg_slot[seg]);
     const uint32_t rows = uniform_u32(s_seg_rows[seg]);
