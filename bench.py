@@ -109,21 +109,24 @@ def union_sizes(cfg, layer, xs, ws):
     return us
 
 
-def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, event_every=0):
+def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, event_every=0, token_major=False):
     """K back-to-back steps between two events on the launch stream.  With
     event_every > 0, every event_every-th step is launched through
     moe_forward_timed, which records an event before and after each stage of
     that step on the same stream (stage durations for the roofline); the other
-    steps run moe_forward unchanged."""
+    steps run moe_forward unchanged.  With token_major, every step runs
+    moe_forward_token_major (no union); its bytes are still counted with the
+    union's U, so GB/s compares the two paths on the same useful work."""
     import torch
     import mixture_experts_decode_gate_amd as moe
     from mixture_experts_decode_gate_amd.hip_events import HipEvent
+    fwd = moe.moe_forward_token_major if token_major else moe.moe_forward
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
     out = torch.empty_like(xs[0])
     nst = moe.moe_num_stages()
     for i in range(warmup):
-        moe.moe_forward(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], out, ws)
+        fwd(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], out, ws)
     traced = [i for i in range(steps) if event_every and i % event_every == 0]
     events = {i: [HipEvent() for _ in range(nst + 1)] for i in traced}
     start, end = HipEvent(), HipEvent()
@@ -135,7 +138,7 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, event_every=0
         if i in events:
             moe.moe_forward_timed(cfg, lay.weights, xs[xi], out, ws, events[i])
         else:
-            moe.moe_forward(cfg, lay.weights, xs[xi], out, ws)
+            fwd(cfg, lay.weights, xs[xi], out, ws)
     end.record(sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -177,10 +180,10 @@ def copy_reference(nbytes=2 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9, ms
 
 
-def cpu_baseline(shape, rows_sample=(0, 1), step=0):
-    """The oracle as it stands, on a bounded sample of the workload: the rows in
-    ``rows_sample`` of one step (routing of all rows, expert FFNs and output for
-    the sampled rows).  Rate = the sample's algorithmic bytes / oracle time."""
+def cpu_baseline(shape, steps=(0, 1, 2)):
+    """The oracle as it stands, on a bounded sample of the workload: every row
+    of the steps in ``steps`` (about 14 s on a 16-core host).  Rate = the
+    sample's algorithmic bytes (each step's own union) / oracle time."""
     import synth
     from oracle.layer import moe_layer_from
     from oracle.route import route
@@ -190,20 +193,24 @@ def cpu_baseline(shape, rows_sample=(0, 1), step=0):
     except Exception:
         threads = 1
     w = synth.layer_weights(shape)
-    x = synth.activations(shape, step)
-    _, ids, _ = route(x, w.router_w, w.bias, shape.route_kind, shape.top_k, shape.norm_topk_prob,
-                      shape.routed_scaling_factor)
-    need = sorted(set(int(e) for r in rows_sample for e in ids[r]))
-    w._experts = {(e, p): synth.expert_tensor(shape, e, p) for e in need for p in range(3)}
-    w.lazy = False
-    t0 = time.perf_counter()
-    moe_layer_from(w, x, rows=list(rows_sample))
-    dt = time.perf_counter() - t0
-    sub = step_bytes(shape, len(rows_sample), len(need))["layer"]
-    return dict(value=sub / dt / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"{shape.name} step {step}, rows {list(rows_sample)} of {shape.rows} "
-                       f"({len(need)} experts + shared), float64 numpy oracle, {dt:.2f} s",
-                seconds=dt, us_per_step=dt * 1e6)
+    dt, nbytes, unions = 0.0, 0, []
+    for step in steps:
+        x = synth.activations(shape, step)
+        _, ids, _ = route(x, w.router_w, w.bias, shape.route_kind, shape.top_k, shape.norm_topk_prob,
+                          shape.routed_scaling_factor)
+        need = sorted(set(int(e) for e in ids.reshape(-1)))
+        # weight generation is not timed: the oracle's input is the decoded layer's storage
+        w._experts = {(e, p): synth.expert_tensor(shape, e, p) for e in need for p in range(3)}
+        w.lazy = False
+        t0 = time.perf_counter()
+        moe_layer_from(w, x)
+        dt += time.perf_counter() - t0
+        nbytes += step_bytes(shape, shape.rows, len(need))["layer"]
+        unions.append(len(need))
+    return dict(value=nbytes / dt / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{shape.name} steps {list(steps)}, all {shape.rows} rows (unions {unions} + shared), "
+                       f"float64 numpy oracle, {dt:.2f} s",
+                seconds=dt, us_per_step=dt * 1e6 / len(steps))
 
 
 def main():
@@ -268,6 +275,25 @@ def main():
                               frac=round(r["gbps"] / HBM_PEAK_GBPS, 4), mean_union=r["mean_union"]))
             log(f"[bench] sweep rows={R}: {r['us_per_step']:.1f} us/step {r['gbps']:.0f} GB/s U={r['mean_union']:.2f}")
 
+    # Union sweep vs token-major (every (row, expert) pair streamed on its own),
+    # on the same inputs: independent rows at rows=1..8, and the correlated
+    # rows=4 verify workload whose mean union is the pages' K=4 figure.
+    ab = []
+    if not args.no_sweep:
+        c3 = synth.CONFIGS["c3_e256_verify4"]
+        cases = [(base_shape.with_rows(R), R, "independent") for R in range(1, 9)] + [(c3, 4, "correlated a=0.58")]
+        for shp, R, kind in cases:
+            xr = [torch.from_numpy(synth.activations(shp, s, rows=R).view(np.int16)).cuda() for s in range(N_INPUTS)]
+            ur = union_sizes(cfg, layers[0], xr, ws)
+            a = timed_run(cfg, layers, xr, ur, shp, R, args.sweep_steps, 10, ws)
+            b = timed_run(cfg, layers, xr, ur, shp, R, args.sweep_steps, 10, ws, token_major=True)
+            ab.append(dict(rows=R, rows_kind=kind, mean_union=a["mean_union"], pairs=R * shp.top_k,
+                           union_us=round(a["us_per_step"], 2), token_major_us=round(b["us_per_step"], 2),
+                           speedup=round(b["us_per_step"] / a["us_per_step"], 4),
+                           expert_streams_saved=round(1 - a["mean_union"] / (R * shp.top_k), 4)))
+            log(f"[bench] A/B rows={R} ({kind}): union {a['us_per_step']:.1f} us (U={a['mean_union']:.2f}) vs "
+                f"token-major {b['us_per_step']:.1f} us ({R * shp.top_k} streams): x{ab[-1]['speedup']:.3f}")
+
     copy_gbps, _ = copy_reference()
     cpu = None
     if not args.no_cpu:
@@ -303,6 +329,7 @@ def main():
         "stages_us": {k: round(v["avg_us"], 2) for k, v in res["stages"].items()},
         "copy_gbps": round(copy_gbps, 1),
         "sweep": sweep,
+        "union_vs_token_major": ab,
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
     }
     print(json.dumps(line), flush=True)

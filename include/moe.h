@@ -199,6 +199,19 @@ moe_status moe_union(const int32_t* topk_ids, int32_t rows, int32_t top_k, int32
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                        uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream);
 
+/* The layer without the union: every (row, selected expert) pair is its own
+ * slot, so an expert chosen by several rows is streamed once per row
+ * (metrale_model_layers/layers/moe/forward_token_major.rs,
+ * MoeLayer::forward_token_major_decode, evaluates the pairs this way).  It is
+ * the baseline the union sweep is measured against ("Function forward_moe"
+ * rustdoc, "RETRACTED (2026-08-29)" note: the same outputs either way).
+ * Arguments, refusals and ownership as moe_forward; ``out`` is byte-identical
+ * to moe_forward's.  The workspace's union fields hold the slot list instead
+ * of the union: union_ids[t] = topk_ids[t], union_count = rows * top_k,
+ * slot_to_union[t] = t, row_mask[t] = 1 << (t / top_k). */
+moe_status moe_forward_token_major(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                                   uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream);
+
 /* moe_forward that also records ``stage_events[i]`` (a hipEvent_t, may be
  * NULL) on ``stream`` before stage i, and ``stage_events[moe_num_stages()]``
  * after the last stage: per-stage timing without changing the work.

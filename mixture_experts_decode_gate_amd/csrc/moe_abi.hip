@@ -216,7 +216,8 @@ void fill_route(moe::RouteParams& p, const moe_config* c, const moe_weights* w, 
 }
 
 moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint16_t* x, uint16_t* out,
-                        int32_t rows, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+                        int32_t rows, void* ws, size_t ws_bytes, void* stream, void* const* events,
+                        bool token_major) {
   moe_status st = check_config(cfg);
   if (st) return st;
   if ((st = check_rows(cfg, rows))) return st;
@@ -232,7 +233,10 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
     if (events && events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s);
     return hipSuccess;
   };
-  const int max_union = cfg->top_k * rows < cfg->num_experts ? cfg->top_k * rows : cfg->num_experts;
+  // Slots the sweeps may see: the union holds at most min(k*rows, E) experts;
+  // the token-major list holds every one of the k*rows pairs.
+  const int max_slots = token_major ? cfg->top_k * rows
+                                    : (cfg->top_k * rows < cfg->num_experts ? cfg->top_k * rows : cfg->num_experts);
 
   moe::RouteParams rp;
   int32_t* ids = reinterpret_cast<int32_t*>(wsb + L.topk_ids);
@@ -254,14 +258,15 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
   sp.seg_slot = sp.seg_count + 1;
   sp.seg_rows = reinterpret_cast<uint32_t*>(sp.seg_slot + moe::kMaxDownSegs);
   sp.seg_cum = reinterpret_cast<int32_t*>(sp.seg_rows + moe::kMaxDownSegs);
+  sp.token_major = token_major ? 1 : 0;
 
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return device_status(e, "event record");
   if ((e = moe::launch_route(rp, false, s)) != hipSuccess) return device_status(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return device_status(e, "event record");
-  if ((e = moe::launch_gateup(sp, rows, max_union, s)) != hipSuccess) return device_status(e, "gate/up launch");
+  if ((e = moe::launch_gateup(sp, rows, max_slots, s)) != hipSuccess) return device_status(e, "gate/up launch");
   if ((e = mark(2)) != hipSuccess) return device_status(e, "event record");
-  if ((e = moe::launch_down(sp, rows, max_union, s)) != hipSuccess) return device_status(e, "down launch");
+  if ((e = moe::launch_down(sp, rows, max_slots, s)) != hipSuccess) return device_status(e, "down launch");
   if ((e = mark(3)) != hipSuccess) return device_status(e, "event record");
   e = moe::launch_blend(sp.y, wts, rp.slot_to_union, reinterpret_cast<const float*>(wsb + L.gamma), out, rows,
                         cfg->hidden, cfg->top_k, s);
@@ -342,13 +347,18 @@ moe_status moe_union(const int32_t* topk_ids, int32_t rows, int32_t top_k, int32
 
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16, uint16_t* out_bf16,
                        int32_t rows, void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, nullptr);
+  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, nullptr, false);
+}
+
+moe_status moe_forward_token_major(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                                   uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, nullptr, true);
 }
 
 moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                              uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream,
                              void* const* stage_events) {
-  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, stage_events);
+  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, stage_events, false);
 }
 
 int32_t moe_num_stages(void) { return kNumStages; }

@@ -59,6 +59,7 @@ struct SweepParams {
   uint32_t* seg_rows;         // [kMaxDownSegs] down segments: packed rows and count
   int32_t* seg_cum;           // [kMaxDownSegs + 1] down segments: weight before segment s
   int32_t* seg_count;         // [1]
+  int token_major;            // 1: one slot per (row, selected expert), no dedup
 };
 
 constexpr size_t kSlotInfoBytes = 72;  // sizeof(SlotInfo), checked in the kernels file
@@ -66,7 +67,7 @@ constexpr size_t kSlotInfoBytes = 72;  // sizeof(SlotInfo), checked in the kerne
 hipError_t launch_route(const RouteParams& p, bool do_topk, hipStream_t s);
 hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids, int32_t* union_count,
                         int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);
-hipError_t launch_gateup(const SweepParams& p, int rows, int max_union, hipStream_t s);
+hipError_t launch_gateup(const SweepParams& p, int rows, int max_slots, hipStream_t s);
 hipError_t launch_down(const SweepParams& p, int rows, int max_union, hipStream_t s);
 hipError_t launch_blend(const float* y, const float* w, const int32_t* slot_to_union, const float* gamma,
                         uint16_t* out, int rows, int h, int k, hipStream_t s);

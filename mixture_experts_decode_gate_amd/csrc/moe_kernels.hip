@@ -87,6 +87,26 @@ __device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows, int la
   return is_first ? pos_self : -1;
 }
 
+// The token-major slot list (MoeLayer::forward_token_major_decode runs every
+// (row, selected expert) pair on its own): slot t = r*k + j holds id[t] for
+// row r alone, so an expert chosen by several rows is swept once per row.
+// Same outputs and return value as union_wave, with U = n.
+__device__ int identity_slots(const int32_t* ids_lds, int n, int k, int lane, int32_t* union_ids,
+                              int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask,
+                              uint32_t* mask_out, int* count_out) {
+  const bool used = lane < n;
+  const uint32_t mask = used ? 1u << (lane / k) : 0u;
+  if (used) {
+    slot_to_union[lane] = lane;
+    union_ids[lane] = ids_lds[lane];
+    row_mask[lane] = mask;
+  }
+  if (lane == 0) *union_count = n;
+  *mask_out = mask;
+  *count_out = n;
+  return used ? lane : -1;
+}
+
 __global__ __launch_bounds__(64) void union_kernel(const int32_t* __restrict__ ids, int rows, int k,
                                                    int32_t* union_ids, int32_t* union_count,
                                                    int32_t* slot_to_union, uint32_t* row_mask) {
@@ -667,7 +687,9 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   if (wave == 0) {
     uint32_t mask;
     int count;
-    const int pos = union_wave(s_ids, R * rp.k, rp.k, R, lane, s_uids, &s_union, s_s2u, s_rmask, &mask, &count);
+    const int pos = p.token_major
+                        ? identity_slots(s_ids, R * rp.k, rp.k, lane, s_uids, &s_union, s_s2u, s_rmask, &mask, &count)
+                        : union_wave(s_ids, R * rp.k, rp.k, R, lane, s_uids, &s_union, s_s2u, s_rmask, &mask, &count);
     if (pos >= 0) {  // lane is the union entry's first slot
       const int ex = s_ids[lane];
       s_slots[pos] = slot_info(kPtab ? s_ptab[ex] : expert_ptrs(rp, ex), ex, rp.inter, mask);
@@ -1157,9 +1179,9 @@ hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids,
   return hipGetLastError();
 }
 
-hipError_t launch_gateup(const SweepParams& p, int rows, int max_union, hipStream_t s) {
+hipError_t launch_gateup(const SweepParams& p, int rows, int max_slots, hipStream_t s) {
   const int nch = (p.h + kChunk - 1) / kChunk;
-  const int max_tiles = max_union * p.inter + p.shared_inter;  // work items (rows)
+  const int max_tiles = max_slots * p.inter + p.shared_inter;  // work items (rows)
   switch (rows) {
     case 1: return gateup_r<1>(p, nch, max_tiles, s);
     case 2: return gateup_r<2>(p, nch, max_tiles, s);

@@ -167,3 +167,31 @@ def test_stage_names():
     assert n >= 1
     assert [lib.moe_stage_name(i) is not None for i in range(n)] == [True] * n
     assert lib.moe_stage_name(n) is None and lib.moe_stage_name(-1) is None
+
+
+def test_token_major_refuses_like_forward():
+    """moe_forward_token_major validates exactly as moe_forward does."""
+    def both(cfg, w, **kw):
+        a = forward(cfg, w, **kw)
+        ws_bytes = kw.pop("ws_bytes", None)
+        if ws_bytes is None:
+            ws_bytes = lib.moe_workspace_bytes(ctypes.byref(cfg)) or 1
+        b = lib.moe_forward_token_major(ctypes.byref(cfg), ctypes.byref(w) if w is not None else None,
+                                        kw.get("x", X), kw.get("out", OUT), kw.get("rows", 4), kw.get("ws", WS),
+                                        ws_bytes, None)
+        return a, b
+
+    cases = [
+        (cfg_c4(hidden=100), fake_weights(), {}),
+        (cfg_c4(), fake_weights(), {"rows": 9}),
+        (cfg_c4(top_k=16), fake_weights(), {"rows": 5}),
+        (cfg_c4(), None, {}),
+        (cfg_c4(), fake_weights(), {"out": X + 64}),
+        (cfg_c4(), fake_weights(sigmoid=False), {}),
+    ]
+    for cfg, w, kw in cases:
+        a, b = both(cfg, w, **kw)
+        assert a == b == moe.MOE_ERR_INVALID_ARG, (kw, a, b)
+    cfg = cfg_c4()
+    need = lib.moe_workspace_bytes(ctypes.byref(cfg))
+    assert both(cfg, fake_weights(), ws_bytes=need - 1) == (moe.MOE_ERR_WORKSPACE, moe.MOE_ERR_WORKSPACE)

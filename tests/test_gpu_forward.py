@@ -236,3 +236,57 @@ def test_graph_capture_replays():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(out_bits(out), eager[rep % 3]), rep
+
+
+# ---------------------------------------------------------------- token-major (no union)
+def run_token_major(dl, x_bits):
+    torch = torch_cuda()
+    moe = moe_mod()
+    x = x_dev(x_bits)
+    out = torch.zeros_like(x)
+    ws = ws_for(dl.cfg)
+    moe.moe_forward_token_major(dl.cfg, dl.weights, x, out, ws)
+    torch.cuda.synchronize()
+    return out_bits(out), ws
+
+
+def check_token_major(dl, x_bits):
+    """The token-major path gives moe_forward's bytes, with the slot list in
+    place of the union: slot t = r*k + j holds id[r, j] for row r alone."""
+    R, k = x_bits.shape[0], dl.cfg.top_k
+    union_out, _ = run_forward(dl, x_bits)
+    tm_out, ws = run_token_major(dl, x_bits)
+    assert np.array_equal(tm_out, union_out)
+    mid = read_intermediates(dl, ws, R)
+    t = np.arange(R * k)
+    assert mid["union_count"] == R * k
+    assert np.array_equal(mid["union_ids"], mid["ids"].reshape(-1))
+    assert np.array_equal(mid["slot_to_union"], t)
+    assert np.array_equal(mid["row_mask"], (1 << (t // k)).astype(np.uint32))
+    return tm_out
+
+
+@pytest.mark.parametrize("name", ["c0_tiny", "c2_e128_verify2"])
+def test_token_major_small_configs(name):
+    shape = synth.CONFIGS[name]
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = synth.activations(shape, 0)
+    got = check_token_major(dl, x)
+    ref = moe_layer_from(weights, x)
+    rel_l2, rel_max = output_errors(got, ref["out"])
+    assert np.all(rel_l2 <= REL_L2_TOL) and np.all(rel_max <= REL_MAX_TOL), (rel_l2, rel_max)
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=[s.name for s in RAGGED])
+def test_token_major_ragged_shapes(shape):
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    check_token_major(dl, synth.activations(shape, 1))
+
+
+def test_token_major_256(layer256):
+    _, dl = layer256
+    for name in ("c3_e256_verify4", "c4_e256_prefill8"):
+        shape = synth.CONFIGS[name]
+        check_token_major(dl, synth.activations(shape, 2))
