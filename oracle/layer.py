@@ -32,7 +32,7 @@ import numpy as np
 from .formats import bf16_to_f64, f32_to_bf16_bits, f64_to_f32
 from .ffn import dequant, ffn_dense
 from .route import route, shared_gate
-from .union import expert_union
+from .union import expert_union, expert_union_local
 
 
 def blend_row(w_row: np.ndarray, y_row: np.ndarray, gamma: float, shared_row: np.ndarray) -> np.ndarray:
@@ -44,10 +44,33 @@ def blend_row(w_row: np.ndarray, y_row: np.ndarray, gamma: float, shared_row: np
     return f32_to_bf16_bits(f64_to_f32(acc))
 
 
+def routed_partial_row(w_row: np.ndarray, y_row: np.ndarray, local: np.ndarray) -> np.ndarray:
+    """fp32(sum_j w[j] * y[j]) over the slots j with ``local[j]``, in float64 in
+    ascending j (zero when no slot is local): one rank's share of the routed
+    sum before the all-reduce (``forward_token_major.rs`` under EP blends with a
+    zeroed shared term, then all-reduces the output)."""
+    acc = np.zeros(y_row.shape[-1], dtype=np.float64)
+    for j in range(len(w_row)):
+        if local[j]:
+            acc = acc + float(w_row[j]) * y_row[j].astype(np.float64)
+    return f64_to_f32(acc)
+
+
+def ep_combine(reduced: np.ndarray, gamma: np.ndarray, shared_y: np.ndarray) -> np.ndarray:
+    """out[r] = bf16(fp32(reduced[r] + gamma[r] * shared[r])): the shared expert
+    added after the all-reduce (``forward_token_major.rs``: ``moe_batched_blend``,
+    or ``residual_add`` with gamma = 1 when the gate weight is null)."""
+    red = np.asarray(reduced, dtype=np.float32).astype(np.float64)
+    s = np.asarray(shared_y, dtype=np.float32).astype(np.float64)
+    g = np.asarray(gamma, dtype=np.float64)[:, None]
+    return f32_to_bf16_bits(f64_to_f32(red + g * s))
+
+
 def moe_layer(x_bits: np.ndarray, *, router_w: np.ndarray, bias: Optional[np.ndarray],
-              shared_gate_vec: np.ndarray, shared: Sequence, expert: Callable[[int, int], object],
+              shared_gate_vec: Optional[np.ndarray], shared: Sequence, expert: Callable[[int, int], object],
               route_kind: int, top_k: int, norm_topk_prob: bool, routed_scaling_factor: float,
-              rows: Optional[Iterable[int]] = None) -> Dict[str, np.ndarray]:
+              rows: Optional[Iterable[int]] = None,
+              expert_range: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """Evaluate the layer on bf16 rows ``x_bits`` [R, h].
 
     ``shared`` is (gate, up, down) NVFP4 matrices; ``expert(e, p)`` returns
@@ -58,6 +81,13 @@ def moe_layer(x_bits: np.ndarray, *, router_w: np.ndarray, bias: Optional[np.nda
     ``slot_to_union``, ``row_mask``, ``y`` (fp32 [R, k, h]; NaN for rows not
     evaluated), ``shared_y`` (fp32 [R, h]) and ``out`` (bf16 bits [R, h];
     0 for rows not evaluated).
+
+    ``shared_gate_vec`` None adds the shared expert ungated (gamma = 1).
+    With ``expert_range`` = (lo, hi) the result also holds one rank's share:
+    ``local_union_ids``, ``local_union_count``, ``local_slot_to_union``,
+    ``local_row_mask`` (``expert_union_local``) and ``partial`` (fp32 [R, h],
+    the routed sum over the row's slots whose expert lies in [lo, hi); NaN for
+    rows not evaluated).
     """
     x_bits = np.atleast_2d(np.asarray(x_bits, dtype=np.uint16))
     R, h = x_bits.shape
@@ -88,12 +118,22 @@ def moe_layer(x_bits: np.ndarray, *, router_w: np.ndarray, bias: Optional[np.nda
     for r in rows:
         out[r] = blend_row(w[r], y[r], gamma[r], shared_y[r])
 
-    return dict(logits=logits, ids=ids, weights=w, gamma=gamma, union_ids=union_ids,
-                union_count=U, slot_to_union=slot_to_union, row_mask=row_mask,
-                y=y, shared_y=shared_y, out=out, rows=np.array(rows, dtype=np.int32))
+    res = dict(logits=logits, ids=ids, weights=w, gamma=gamma, union_ids=union_ids,
+               union_count=U, slot_to_union=slot_to_union, row_mask=row_mask,
+               y=y, shared_y=shared_y, out=out, rows=np.array(rows, dtype=np.int32))
+    if expert_range is not None:
+        lo, hi = int(expert_range[0]), int(expert_range[1])
+        lu, lU, ls2u, lmask = expert_union_local(ids, lo, hi)
+        partial = np.full((R, h), np.nan, dtype=np.float32)
+        for r in rows:
+            partial[r] = routed_partial_row(w[r], y[r], (ids[r] >= lo) & (ids[r] < hi))
+        res.update(local_union_ids=lu, local_union_count=lU, local_slot_to_union=ls2u, local_row_mask=lmask,
+                   partial=partial)
+    return res
 
 
-def moe_layer_from(weights, x_bits: np.ndarray, rows: Optional[Iterable[int]] = None) -> Dict[str, np.ndarray]:
+def moe_layer_from(weights, x_bits: np.ndarray, rows: Optional[Iterable[int]] = None,
+                   expert_range: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """Convenience wrapper: ``weights`` has router_w, bias, shared_gate_vec, shared,
     expert(e, p) and a ``shape`` with the routing parameters."""
     s = weights.shape
@@ -101,4 +141,4 @@ def moe_layer_from(weights, x_bits: np.ndarray, rows: Optional[Iterable[int]] = 
                      shared_gate_vec=weights.shared_gate_vec, shared=weights.shared,
                      expert=weights.expert, route_kind=s.route_kind, top_k=s.top_k,
                      norm_topk_prob=s.norm_topk_prob, routed_scaling_factor=s.routed_scaling_factor,
-                     rows=rows)
+                     rows=rows, expert_range=expert_range)

@@ -46,9 +46,15 @@ def router_logits(x_bits: np.ndarray, router_w: np.ndarray) -> np.ndarray:
     return f64_to_f32(x @ w.T)
 
 
-def shared_gate(x_bits: np.ndarray, gate_vec: np.ndarray) -> np.ndarray:
-    """gamma[r] = sigmoid(x_r . g_s) in float64: the shared expert's blend gate."""
+def shared_gate(x_bits: np.ndarray, gate_vec) -> np.ndarray:
+    """gamma[r] = sigmoid(x_r . g_s) in float64: the shared expert's blend gate.
+
+    Without a gate vector (``None``) the shared expert is added ungated,
+    gamma = 1: ``forward_token_major.rs`` calls ``residual_add`` instead of
+    ``moe_batched_blend`` when ``shared_expert_gate.weight`` is null."""
     x = bf16_to_f64(x_bits)
+    if gate_vec is None:
+        return np.ones(x.shape[0], dtype=np.float64)
     z = x @ np.asarray(gate_vec, dtype=np.float32).astype(np.float64)
     return 1.0 / (1.0 + np.exp(-z))
 

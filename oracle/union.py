@@ -48,3 +48,37 @@ def expert_union(ids: np.ndarray) -> Tuple[np.ndarray, int, np.ndarray, np.ndarr
         row_mask[slot_to_union[t]] |= 1 << (t // k)
     return (np.array(union_ids, dtype=np.int32), U,
             np.array(slot_to_union, dtype=np.int32), np.array(row_mask, dtype=np.uint32))
+
+
+def expert_union_local(ids: np.ndarray, lo: int, hi: int) -> Tuple[np.ndarray, int, np.ndarray, np.ndarray]:
+    """The union of the selected experts that lie in [lo, hi): one GPU's share
+    under expert parallelism.
+
+    ``forward_ep.rs`` (``MoeLayer::forward_ep_dispatch``) splits a token's
+    selected ids into local and remote ones with ``local_expert_range`` and
+    ``build_ep_routing_table``; the rank sweeps only its local experts.  Here:
+    slots whose id is outside [lo, hi) are skipped (``slot_to_union[t] = -1``);
+    the others form the union exactly as in ``expert_union`` (first occurrence
+    in row-major slot order among the local slots).
+    """
+    ids = np.asarray(ids)
+    R, k = ids.shape
+    flat = [int(v) for v in ids.reshape(-1)]
+    union_ids = []
+    slot_to_union = [-1] * len(flat)
+    for t, e in enumerate(flat):
+        if not (lo <= e < hi):
+            continue
+        earlier = [t2 for t2 in range(t) if flat[t2] == e]
+        if earlier:
+            slot_to_union[t] = slot_to_union[earlier[0]]
+        else:
+            slot_to_union[t] = len(union_ids)
+            union_ids.append(e)
+    U = len(union_ids)
+    row_mask = [0] * U
+    for t, u in enumerate(slot_to_union):
+        if u >= 0:
+            row_mask[u] |= 1 << (t // k)
+    return (np.array(union_ids, dtype=np.int32), U,
+            np.array(slot_to_union, dtype=np.int32), np.array(row_mask, dtype=np.uint32))

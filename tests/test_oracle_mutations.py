@@ -3,7 +3,9 @@
 Each case patches one plausible error into the oracle (swapped nibbles, an
 exponent bias off by one, silu on the wrong projection, a dropped shared
 term, ties broken the wrong way, a sorted union, renormalising over all
-experts, biased sigmoid weights) and runs the pin that should catch it.
+experts, biased sigmoid weights, a local union without its range filter, a
+rank's partial that keeps remote slots, an ungated shared expert dropped) and
+runs the pin that should catch it.
 """
 
 import numpy as np
@@ -136,3 +138,34 @@ def test_biased_sigmoid_weights_caught(monkeypatch):
     monkeypatch.setattr(RT, "topk_sigmoid_bias", _biased_weights)
     with pytest.raises(AssertionError):
         T_route.test_sigmoid_weights_are_unbiased_scores()
+
+
+def _local_union_keeps_remote(ids, lo, hi):
+    # the mistake: the range filter is dropped, every selected id stays local
+    return UN.expert_union(ids)
+
+
+def test_local_union_without_range_filter_caught(monkeypatch):
+    monkeypatch.setattr(T_union, "expert_union_local", _local_union_keeps_remote)
+    with pytest.raises(AssertionError):
+        T_union.test_local_union_exhaustive_tiny()
+
+
+def test_partial_with_remote_slots_caught(monkeypatch):
+    real = LY.routed_partial_row
+    # the mistake: every slot counts as local
+    monkeypatch.setattr(LY, "routed_partial_row", lambda w_row, y_row, local: real(w_row, y_row, np.ones_like(local)))
+    with pytest.raises(AssertionError):
+        T_layer.test_ep_partial_single_expert_closed_form()
+
+
+def test_ungated_shared_as_zero_caught(monkeypatch):
+    real = RT.shared_gate
+
+    def zero_when_ungated(x_bits, gate_vec):
+        if gate_vec is None:
+            return np.zeros(np.atleast_2d(x_bits).shape[0])
+        return real(x_bits, gate_vec)
+    monkeypatch.setattr(LY, "shared_gate", zero_when_ungated)
+    with pytest.raises(AssertionError):
+        T_layer.test_ungated_shared_expert_is_gate_one()

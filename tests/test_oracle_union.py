@@ -65,3 +65,58 @@ def test_union_random_large():
         R = min(R, 8)
         ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(R)])
         _check(ids)
+
+
+# ---------------------------------------------------------------- one rank's share (expert parallel)
+from oracle.union import expert_union_local  # noqa: E402
+
+
+def _check_local(ids, lo, hi):
+    ids = np.asarray(ids)
+    R, k = ids.shape
+    flat = ids.reshape(-1).tolist()
+    u, U, s2u, mask = expert_union_local(ids, lo, hi)
+    ref = list(dict.fromkeys(e for e in flat if lo <= e < hi))   # insertion-ordered dedup of the local ids
+    assert u.tolist() == ref and U == len(ref)
+    for t, e in enumerate(flat):
+        if lo <= e < hi:
+            assert u[s2u[t]] == e
+        else:
+            assert s2u[t] == -1
+    for i, e in enumerate(ref):
+        assert int(mask[i]) == sum(1 << (t // k) for t, v in enumerate(flat) if v == e)
+
+
+def test_local_union_exhaustive_tiny():
+    n = 0
+    for E in range(1, 6):
+        for k in range(1, min(E, 3) + 1):
+            row_choices = list(itertools.permutations(range(E), k))
+            for R in range(1, 3):
+                for rows in itertools.product(row_choices, repeat=R):
+                    for lo in range(E + 1):
+                        for hi in range(lo, E + 1):
+                            _check_local(np.array(rows), lo, hi)
+                            n += 1
+    assert n > 5000
+
+
+def test_local_unions_partition_the_union():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        E = int(rng.integers(8, 300))
+        k = int(rng.integers(1, 9))
+        R = min(8, int(rng.integers(1, 64 // k + 1)))
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(R)])
+        gu, GU, gs2u, gmask = expert_union(ids)
+        # the whole range is the union itself
+        lu, lU, ls2u, lmask = expert_union_local(ids, 0, E)
+        assert lU == GU and np.array_equal(lu, gu) and np.array_equal(ls2u, gs2u) and np.array_equal(lmask, gmask)
+        # G contiguous ranges: disjoint local unions that cover the union, each slot local to one rank
+        G = int(rng.integers(2, 9))
+        cuts = [0] + sorted(rng.choice(np.arange(1, E), size=min(G - 1, E - 1), replace=False).tolist()) + [E]
+        parts = [expert_union_local(ids, a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+        assert sum(p[1] for p in parts) == GU
+        assert set().union(*[set(p[0].tolist()) for p in parts]) == set(gu.tolist())
+        owners = np.sum([p[2] >= 0 for p in parts], axis=0)
+        assert np.all(owners == 1)
