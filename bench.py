@@ -160,6 +160,42 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, event_every=0
     return res
 
 
+def ep_shares(cfg, layers, xs, shape, rows, n_ranks, steps, ws):
+    """Time moe_forward_ep_partial for each of n_ranks equal expert ranges."""
+    import torch
+    import mixture_experts_decode_gate_amd as moe
+    from mixture_experts_decode_gate_amd.hip_events import HipEvent
+    E = shape.num_experts
+    L = moe.moe_workspace_layout(cfg)
+    partial = torch.empty((rows, shape.hidden), dtype=torch.float32, device="cuda")
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    out = []
+    for g in range(n_ranks):
+        lo, hi = g * E // n_ranks, (g + 1) * E // n_ranks
+        us = []
+        for x in xs:
+            moe.moe_forward_ep_partial(cfg, layers[0].weights, x, partial, lo, hi, ws)
+            torch.cuda.synchronize()
+            us.append(int(ws[L.union_count:L.union_count + 4].cpu().numpy().view(np.int32)[0]))
+        for i in range(10):
+            moe.moe_forward_ep_partial(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], partial, lo, hi, ws)
+        e0, e1 = HipEvent(), HipEvent()
+        torch.cuda.synchronize()
+        e0.record(sh)
+        for i in range(steps):
+            moe.moe_forward_ep_partial(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], partial, lo, hi, ws)
+        e1.record(sh)
+        torch.cuda.synchronize()
+        t_us = e0.elapsed_ms(e1) * 1e3 / steps
+        mean_u = float(np.mean([us[i % len(xs)] for i in range(steps)]))
+        nbytes = step_bytes(shape, rows, mean_u)["layer"]
+        out.append(dict(lo=lo, hi=hi, mean_local_union=round(mean_u, 3), us_per_step=round(t_us, 2),
+                        gbps=round(nbytes / (t_us * 1e-6) / 1e9, 1)))
+    return dict(rows=rows, ranks=n_ranks, ranges=out, slowest_us=max(r["us_per_step"] for r in out),
+                note="per-range time of moe_forward_ep_partial (local union + shared expert + fp32 partial); "
+                     "all-reduce and combine not included")
+
+
 def copy_reference(nbytes=2 << 30, reps=10):
     """Achieved bandwidth of a plain device copy (read + write), for context."""
     import torch
@@ -294,6 +330,18 @@ def main():
             log(f"[bench] A/B rows={R} ({kind}): union {a['us_per_step']:.1f} us (U={a['mean_union']:.2f}) vs "
                 f"token-major {b['us_per_step']:.1f} us ({R * shp.top_k} streams): x{ab[-1]['speedup']:.3f}")
 
+    # One GPU's expert-parallel share at the real shape: the layer's 256
+    # experts split over 8 GPUs, each sweeping its 32-expert range of the
+    # union (plus the shared expert) and writing an fp32 partial.  Each range is
+    # timed on its own; the slowest sets an 8-GPU step (the all-reduce is not
+    # part of the library and not timed).
+    ep = None
+    if not args.no_sweep:
+        ep = ep_shares(cfg, layers, xs, shape, args.rows, 8, args.sweep_steps, ws)
+        log(f"[bench] EP share rows={args.rows}, 8 ranges of {shape.num_experts // 8} experts: "
+            f"local unions {[r['mean_local_union'] for r in ep['ranges']]}, "
+            f"us {[r['us_per_step'] for r in ep['ranges']]}")
+
     copy_gbps, _ = copy_reference()
     cpu = None
     if not args.no_cpu:
@@ -330,6 +378,7 @@ def main():
         "copy_gbps": round(copy_gbps, 1),
         "sweep": sweep,
         "union_vs_token_major": ab,
+        "ep_share": ep,
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
     }
     print(json.dumps(line), flush=True)

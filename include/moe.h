@@ -35,6 +35,7 @@
  *   FFN_e(x) = W_down[e] @ (silu(W_gate[e] @ x) * (W_up[e] @ x))
  *   out[r]   = bf16( sum_j w[r,j] * FFN_{ids[r,j]}(x_r)
  *                    + sigmoid(x_r . shared_expert_gate) * FFN_shared(x_r) )
+ *            (gate 1 when shared_expert_gate is NULL)
  *
  * NVFP4 matrix [n, k] ("untransposed": k contiguous):
  *   packed  uint8 [n, k/2]   two E2M1 codes per byte, even column in the low nibble
@@ -128,7 +129,10 @@ typedef struct moe_weights {
   moe_nvfp4 shared_gate;           /* [Is, h]                                    */
   moe_nvfp4 shared_up;             /* [Is, h]                                    */
   moe_nvfp4 shared_down;           /* [h, Is]                                    */
-  const float* shared_expert_gate; /* [h] fp32: gate = sigmoid(x . this)        */
+  const float* shared_expert_gate; /* [h] fp32: gate = sigmoid(x . this); NULL:
+                                      the shared expert is added ungated (gate 1),
+                                      as forward_token_major.rs does with
+                                      residual_add when the gate weight is null */
 } moe_weights;
 
 /* Byte offsets of the intermediates moe_forward leaves in the workspace.
@@ -191,6 +195,16 @@ moe_status moe_union(const int32_t* topk_ids, int32_t rows, int32_t top_k, int32
                      int32_t* union_ids, int32_t* union_count, int32_t* slot_to_union,
                      uint32_t* row_mask, void* stream);
 
+/* moe_union restricted to the experts in [expert_lo, expert_hi): one GPU's
+ * share under expert parallelism (forward_ep.rs splits the selected ids into
+ * local and remote ones by local_expert_range and build_ep_routing_table).
+ * Slots whose id is outside the range get slot_to_union = -1 and are not in
+ * the union; the others form it as moe_union does.  Arguments and refusals
+ * as moe_union, plus 0 <= expert_lo <= expert_hi <= num_experts. */
+moe_status moe_union_local(const int32_t* topk_ids, int32_t rows, int32_t top_k, int32_t num_experts,
+                           int32_t expert_lo, int32_t expert_hi, int32_t* union_ids, int32_t* union_count,
+                           int32_t* slot_to_union, uint32_t* row_mask, void* stream);
+
 /* The whole layer: x[rows, h] bf16 -> out[rows, h] bf16 (overwritten, not
  * accumulated).  x and out 16-byte aligned and not overlapping.  Leaves every
  * intermediate of moe_ws_layout in the workspace.  Each row's output depends
@@ -211,6 +225,35 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16
  * slot_to_union[t] = t, row_mask[t] = 1 << (t / top_k). */
 moe_status moe_forward_token_major(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                                    uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream);
+
+/* One GPU's share of the layer under expert parallelism, before the
+ * all-reduce (forward_token_major.rs under EP: the weighted sum is blended
+ * with a zeroed shared term, then the output is all-reduced across ranks).
+ * Every GPU routes all rows identically; this one sweeps only the union
+ * experts in [expert_lo, expert_hi) and writes
+ *   partial[r][n] = fp32( sum over j with expert_lo <= ids[r,j] < expert_hi
+ *                         of w[r,j] * FFN_{ids[r,j]}(x_r)[n] )   (ascending j)
+ *   partial  [rows, h] fp32 out, 16-byte aligned, overwritten.
+ * It also runs the shared expert and leaves it, and the gate, in the
+ * workspace for moe_ep_combine.  The expert tables are indexed by global
+ * expert id; entries outside the range are read but never dereferenced.
+ * Refusals as moe_forward, plus 0 <= expert_lo <= expert_hi <= num_experts.
+ * The workspace's union fields hold the local union (moe_union_local). */
+moe_status moe_forward_ep_partial(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                                  float* partial, int32_t rows, int32_t expert_lo, int32_t expert_hi, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/* After the caller's all-reduce of the ranks' partials (the reduce itself is
+ * not part of this library): the shared expert added to the reduced routed
+ * sum, as forward_token_major.rs does with moe_batched_blend (or residual_add,
+ * gate 1, when shared_expert_gate is NULL):
+ *   out[r][n] = bf16( reduced[r][n] + gate_r * FFN_shared(x_r)[n] )
+ *   reduced  [rows, h] fp32 in, 16-byte aligned
+ *   out      [rows, h] bf16 out, 16-byte aligned, overwritten
+ * ``ws`` must hold what moe_forward_ep_partial left in it for the same x and
+ * rows (same stream, no other call on the workspace in between). */
+moe_status moe_ep_combine(const moe_config* cfg, const float* reduced, uint16_t* out_bf16, int32_t rows, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /* moe_forward that also records ``stage_events[i]`` (a hipEvent_t, may be
  * NULL) on ``stream`` before stage i, and ``stage_events[moe_num_stages()]``

@@ -10,6 +10,9 @@ libmoe.so.  The names match the C ABI in include/moe.h:
     moe_forward(cfg, w, x, out, ws)                  the whole layer
     moe_forward_token_major(cfg, w, x, out, ws)      the layer without the union (one slot per pair)
     moe_forward_timed(cfg, w, x, out, ws, events)    same, with per-stage events
+    moe_union_local(topk_ids, lo, hi, union_ids, union_count, slot_to_union, row_mask, num_experts)
+    moe_forward_ep_partial(cfg, w, x, partial, lo, hi, ws)   one GPU's expert-parallel share
+    moe_ep_combine(cfg, reduced, out, ws)            shared expert added after the reduce
 
 Tensors are torch CUDA (HIP) tensors; torch only provides device memory and
 the current stream.  There is no CPU fallback: loading fails loudly when the
@@ -105,6 +108,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward.restype = C.c_int
     lib.moe_forward_token_major.argtypes = lib.moe_forward.argtypes
     lib.moe_forward_token_major.restype = C.c_int
+    lib.moe_union_local.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.moe_union_local.restype = C.c_int
+    lib.moe_forward_ep_partial.argtypes = [P(MoeConfig), P(MoeWeights), C.c_void_p, C.c_void_p, C.c_int32,
+                                           C.c_int32, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.moe_forward_ep_partial.restype = C.c_int
+    lib.moe_ep_combine.argtypes = [P(MoeConfig), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
+                                   C.c_void_p]
+    lib.moe_ep_combine.restype = C.c_int
     lib.moe_forward_timed.argtypes = [P(MoeConfig), P(MoeWeights), C.c_void_p, C.c_void_p, C.c_int32,
                                       C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
     lib.moe_forward_timed.restype = C.c_int
@@ -168,6 +180,27 @@ def moe_forward_token_major(cfg: MoeConfig, w: MoeWeights, x, out, ws, stream=No
     """moe_forward with one slot per (row, selected expert) instead of the union."""
     _check(load().moe_forward_token_major(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(x.shape[0]),
                                           _ptr(ws), int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def moe_union_local(topk_ids, lo: int, hi: int, union_ids, union_count, slot_to_union, row_mask=None,
+                    num_experts: int = MOE_MAX_EXPERTS, stream=None) -> None:
+    """moe_union over the ids in [lo, hi) only; other slots map to -1."""
+    rows, k = int(topk_ids.shape[0]), int(topk_ids.shape[1])
+    _check(load().moe_union_local(_ptr(topk_ids), rows, k, int(num_experts), int(lo), int(hi), _ptr(union_ids),
+                                  _ptr(union_count), _ptr(slot_to_union), _ptr(row_mask), _stream(stream)))
+
+
+def moe_forward_ep_partial(cfg: MoeConfig, w: MoeWeights, x, partial, lo: int, hi: int, ws, stream=None) -> None:
+    """x [rows, h] bf16 -> partial [rows, h] float32: the routed sum over experts in [lo, hi)."""
+    _check(load().moe_forward_ep_partial(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(partial),
+                                         int(x.shape[0]), int(lo), int(hi), _ptr(ws),
+                                         int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def moe_ep_combine(cfg: MoeConfig, reduced, out, ws, stream=None) -> None:
+    """reduced [rows, h] float32 -> out [rows, h] bf16 = reduced + gate * shared expert."""
+    _check(load().moe_ep_combine(ctypes.byref(cfg), _ptr(reduced), _ptr(out), int(reduced.shape[0]), _ptr(ws),
+                                 int(ws.numel() * ws.element_size()), _stream(stream)))
 
 
 def moe_forward_timed(cfg: MoeConfig, w: MoeWeights, x, out, ws, events: Sequence, stream=None) -> None:

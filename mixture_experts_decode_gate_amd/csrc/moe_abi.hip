@@ -105,9 +105,8 @@ moe_status check_route_weights(const moe_config* c, const moe_weights* w) {
   } else if (w->correction_bias) {
     return fail(MOE_ERR_INVALID_ARG, "softmax routing takes no correction_bias");
   }
-  if (!w->shared_expert_gate)
-    return fail(MOE_ERR_UNSUPPORTED, "shared_expert_gate is NULL (ungated shared expert not served)");
-  if (!aligned(w->shared_expert_gate, 16))
+  // A NULL gate is the ungated shared expert (gamma = 1).
+  if (w->shared_expert_gate && !aligned(w->shared_expert_gate, 16))
     return fail(MOE_ERR_INVALID_ARG, "shared_expert_gate must be 16-byte aligned");
   return MOE_OK;
 }
@@ -173,6 +172,30 @@ moe_status check_xy(const moe_config* c, const uint16_t* x, const uint16_t* out,
   return MOE_OK;
 }
 
+moe_status check_union_args(const int32_t* topk_ids, int32_t rows, int32_t top_k, int32_t num_experts,
+                            const int32_t* union_ids, const int32_t* union_count, const int32_t* slot_to_union,
+                            const uint32_t* row_mask) {
+  if (rows < 1 || rows > MOE_MAX_ROWS) return fail(MOE_ERR_INVALID_ARG, "rows=%d outside [1, %d]", rows, MOE_MAX_ROWS);
+  if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts=%d outside [1, %d]", num_experts, MOE_MAX_EXPERTS);
+  if (top_k < 1 || top_k > num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside [1, num_experts=%d]", top_k, num_experts);
+  if (top_k * rows > MOE_MAX_IDS)
+    return fail(MOE_ERR_INVALID_ARG, "top_k*rows=%d exceeds %d", top_k * rows, MOE_MAX_IDS);
+  if (!topk_ids || !union_ids || !union_count || !slot_to_union)
+    return fail(MOE_ERR_INVALID_ARG, "NULL id buffer");
+  if (!aligned(topk_ids, 4) || !aligned(union_ids, 4) || !aligned(union_count, 4) || !aligned(slot_to_union, 4) ||
+      (row_mask && !aligned(row_mask, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "id buffers must be 4-byte aligned");
+  const size_t n = (size_t)rows * top_k * 4;
+  if (overlaps(union_ids, MOE_MAX_IDS * 4, slot_to_union, n) || overlaps(union_count, 4, union_ids, MOE_MAX_IDS * 4) ||
+      overlaps(union_count, 4, slot_to_union, n) ||
+      (row_mask && (overlaps(row_mask, MOE_MAX_IDS * 4, union_ids, MOE_MAX_IDS * 4) ||
+                    overlaps(row_mask, MOE_MAX_IDS * 4, slot_to_union, n) || overlaps(row_mask, MOE_MAX_IDS * 4, union_count, 4))))
+    return fail(MOE_ERR_INVALID_ARG, "union output buffers overlap");
+  return MOE_OK;
+}
+
 moe_status device_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
   return MOE_OK;
@@ -183,7 +206,12 @@ void fill_route(moe::RouteParams& p, const moe_config* c, const moe_weights* w, 
   memset(&p, 0, sizeof p);
   p.x = x;
   p.router_w = w->router_w;
-  p.gate_vec = w->shared_expert_gate;
+  // Without a gate vector the gate pass reads the router's first row (any h
+  // readable floats) and writes gamma = 1.
+  p.gate_vec = w->shared_expert_gate ? w->shared_expert_gate : w->router_w;
+  p.ungated = w->shared_expert_gate ? 0 : 1;
+  p.expert_lo = 0;
+  p.expert_hi = c->num_experts;
   p.h = c->hidden;
   // Top-k reads bias[e] unconditionally; softmax routing ignores the value,
   // so it reads the router weights (at least E floats) there instead.
@@ -215,17 +243,36 @@ void fill_route(moe::RouteParams& p, const moe_config* c, const moe_weights* w, 
   p.shared_inter = c->shared_inter;
 }
 
+// Options of one layer evaluation beyond moe_forward's arguments.
+struct ForwardMode {
+  bool token_major = false;  // one slot per (row, selected expert), no union
+  int lo = 0, hi = -1;       // experts swept: [lo, hi) (hi < 0: all)
+  float* partial = nullptr;  // EP share: fp32 routed partial instead of out
+};
+
 moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint16_t* x, uint16_t* out,
                         int32_t rows, void* ws, size_t ws_bytes, void* stream, void* const* events,
-                        bool token_major) {
+                        const ForwardMode& mode) {
   moe_status st = check_config(cfg);
   if (st) return st;
   if ((st = check_rows(cfg, rows))) return st;
   if ((st = check_all_weights(cfg, w))) return st;
   moe_ws_layout L;
   if ((st = check_ws(cfg, ws, ws_bytes, &L))) return st;
-  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
-  if ((st = check_xy(cfg, x, out, rows, ws, L))) return st;
+  const int lo = mode.lo, hi = mode.hi < 0 ? cfg->num_experts : mode.hi;
+  if (lo < 0 || lo > hi || hi > cfg->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "expert range [%d, %d) outside [0, num_experts=%d]", lo, hi, cfg->num_experts);
+  if (mode.partial) {
+    const size_t pb = (size_t)rows * cfg->hidden * sizeof(float);
+    if (!aligned(mode.partial, 16)) return fail(MOE_ERR_INVALID_ARG, "partial must be 16-byte aligned");
+    if (overlaps(mode.partial, pb, x, (size_t)rows * cfg->hidden * 2) || overlaps(mode.partial, pb, ws, L.total))
+      return fail(MOE_ERR_INVALID_ARG, "partial overlaps x or the workspace");
+    if ((st = check_xy(cfg, x, nullptr, rows, ws, L))) return st;
+  } else {
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    if ((st = check_xy(cfg, x, out, rows, ws, L))) return st;
+  }
+  const bool token_major = mode.token_major;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
@@ -235,13 +282,14 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
   };
   // Slots the sweeps may see: the union holds at most min(k*rows, E) experts;
   // the token-major list holds every one of the k*rows pairs.
-  const int max_slots = token_major ? cfg->top_k * rows
-                                    : (cfg->top_k * rows < cfg->num_experts ? cfg->top_k * rows : cfg->num_experts);
+  const int max_slots = token_major ? cfg->top_k * rows : (cfg->top_k * rows < hi - lo ? cfg->top_k * rows : hi - lo);
 
   moe::RouteParams rp;
   int32_t* ids = reinterpret_cast<int32_t*>(wsb + L.topk_ids);
   float* wts = reinterpret_cast<float*>(wsb + L.topk_w);
   fill_route(rp, cfg, w, x, rows, wsb, L, ids, wts);
+  rp.expert_lo = lo;
+  rp.expert_hi = hi;
 
   moe::SweepParams sp;
   sp.x = x;
@@ -268,8 +316,8 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
   if ((e = mark(2)) != hipSuccess) return device_status(e, "event record");
   if ((e = moe::launch_down(sp, rows, max_slots, s)) != hipSuccess) return device_status(e, "down launch");
   if ((e = mark(3)) != hipSuccess) return device_status(e, "event record");
-  e = moe::launch_blend(sp.y, wts, rp.slot_to_union, reinterpret_cast<const float*>(wsb + L.gamma), out, rows,
-                        cfg->hidden, cfg->top_k, s);
+  e = moe::launch_blend(sp.y, wts, rp.slot_to_union, reinterpret_cast<const float*>(wsb + L.gamma), out,
+                        mode.partial, rows, cfg->hidden, cfg->top_k, s);
   if (e != hipSuccess) return device_status(e, "blend launch");
   if ((e = mark(4)) != hipSuccess) return device_status(e, "event record");
   return ok();
@@ -321,44 +369,77 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t
 moe_status moe_union(const int32_t* topk_ids, int32_t rows, int32_t top_k, int32_t num_experts,
                      int32_t* union_ids, int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask,
                      void* stream) {
-  if (rows < 1 || rows > MOE_MAX_ROWS) return fail(MOE_ERR_INVALID_ARG, "rows=%d outside [1, %d]", rows, MOE_MAX_ROWS);
-  if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS)
-    return fail(MOE_ERR_INVALID_ARG, "num_experts=%d outside [1, %d]", num_experts, MOE_MAX_EXPERTS);
-  if (top_k < 1 || top_k > num_experts)
-    return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside [1, num_experts=%d]", top_k, num_experts);
-  if (top_k * rows > MOE_MAX_IDS)
-    return fail(MOE_ERR_INVALID_ARG, "top_k*rows=%d exceeds %d", top_k * rows, MOE_MAX_IDS);
-  if (!topk_ids || !union_ids || !union_count || !slot_to_union)
-    return fail(MOE_ERR_INVALID_ARG, "NULL id buffer");
-  if (!aligned(topk_ids, 4) || !aligned(union_ids, 4) || !aligned(union_count, 4) || !aligned(slot_to_union, 4) ||
-      (row_mask && !aligned(row_mask, 4)))
-    return fail(MOE_ERR_INVALID_ARG, "id buffers must be 4-byte aligned");
-  const size_t n = (size_t)rows * top_k * 4;
-  if (overlaps(union_ids, MOE_MAX_IDS * 4, slot_to_union, n) || overlaps(union_count, 4, union_ids, MOE_MAX_IDS * 4) ||
-      overlaps(union_count, 4, slot_to_union, n) ||
-      (row_mask && (overlaps(row_mask, MOE_MAX_IDS * 4, union_ids, MOE_MAX_IDS * 4) ||
-                    overlaps(row_mask, MOE_MAX_IDS * 4, slot_to_union, n) || overlaps(row_mask, MOE_MAX_IDS * 4, union_count, 4))))
-    return fail(MOE_ERR_INVALID_ARG, "union output buffers overlap");
+  moe_status st = check_union_args(topk_ids, rows, top_k, num_experts, union_ids, union_count, slot_to_union, row_mask);
+  if (st) return st;
   hipError_t e = moe::launch_union(topk_ids, rows, top_k, union_ids, union_count, slot_to_union, row_mask,
                                    reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_status(e, "union launch");
   return ok();
 }
 
+moe_status moe_union_local(const int32_t* topk_ids, int32_t rows, int32_t top_k, int32_t num_experts,
+                           int32_t expert_lo, int32_t expert_hi, int32_t* union_ids, int32_t* union_count,
+                           int32_t* slot_to_union, uint32_t* row_mask, void* stream) {
+  moe_status st = check_union_args(topk_ids, rows, top_k, num_experts, union_ids, union_count, slot_to_union, row_mask);
+  if (st) return st;
+  if (expert_lo < 0 || expert_lo > expert_hi || expert_hi > num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "expert range [%d, %d) outside [0, num_experts=%d]", expert_lo, expert_hi,
+                num_experts);
+  hipError_t e = moe::launch_union_local(topk_ids, rows, top_k, expert_lo, expert_hi, union_ids, union_count,
+                                         slot_to_union, row_mask, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_status(e, "union launch");
+  return ok();
+}
+
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16, uint16_t* out_bf16,
                        int32_t rows, void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, nullptr, false);
+  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, nullptr, ForwardMode());
 }
 
 moe_status moe_forward_token_major(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                                    uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, nullptr, true);
+  ForwardMode m;
+  m.token_major = true;
+  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, nullptr, m);
+}
+
+moe_status moe_forward_ep_partial(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                                  float* partial, int32_t rows, int32_t expert_lo, int32_t expert_hi, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  if (!partial) return fail(MOE_ERR_INVALID_ARG, "partial is NULL");
+  ForwardMode m;
+  m.lo = expert_lo;
+  m.hi = expert_hi;
+  m.partial = partial;
+  if (expert_hi < 0) return fail(MOE_ERR_INVALID_ARG, "expert_hi=%d is negative", expert_hi);
+  return forward_impl(cfg, w, x_bf16, nullptr, rows, ws, ws_bytes, stream, nullptr, m);
+}
+
+moe_status moe_ep_combine(const moe_config* cfg, const float* reduced, uint16_t* out_bf16, int32_t rows, void* ws,
+                          size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_rows(cfg, rows))) return st;
+  moe_ws_layout L;
+  if ((st = check_ws(cfg, ws, ws_bytes, &L))) return st;
+  const size_t rb = (size_t)rows * cfg->hidden * sizeof(float), ob = (size_t)rows * cfg->hidden * 2;
+  if (!reduced || !aligned(reduced, 16)) return fail(MOE_ERR_INVALID_ARG, "reduced must be a 16-byte aligned pointer");
+  if (!out_bf16 || !aligned(out_bf16, 16)) return fail(MOE_ERR_INVALID_ARG, "out must be a 16-byte aligned pointer");
+  if (overlaps(reduced, rb, out_bf16, ob)) return fail(MOE_ERR_INVALID_ARG, "reduced and out overlap");
+  if (overlaps(reduced, rb, ws, L.total) || overlaps(out_bf16, ob, ws, L.total))
+    return fail(MOE_ERR_INVALID_ARG, "reduced or out overlaps the workspace");
+  char* wsb = static_cast<char*>(ws);
+  hipError_t e = moe::launch_ep_combine(reduced, reinterpret_cast<const float*>(wsb + L.y),
+                                        reinterpret_cast<const float*>(wsb + L.gamma), out_bf16, rows, cfg->hidden,
+                                        reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_status(e, "combine launch");
+  return ok();
 }
 
 moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                              uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream,
                              void* const* stage_events) {
-  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, stage_events, false);
+  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, stage_events, ForwardMode());
 }
 
 int32_t moe_num_stages(void) { return kNumStages; }

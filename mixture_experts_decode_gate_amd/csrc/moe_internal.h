@@ -39,6 +39,8 @@ struct RouteParams {
   int32_t* slot_to_union;
   uint32_t* row_mask;
   SlotInfo* slots;         // [65]
+  int expert_lo, expert_hi; // experts swept: the union keeps ids in [lo, hi) (all of [0, E) but under EP)
+  int ungated;             // 1: no shared-expert gate vector, gamma = 1 (gate_vec then points at any h floats)
   moe_expert_table gate, up, down;
   moe_nvfp4 shared_gate, shared_up, shared_down;
   int inter, shared_inter;
@@ -69,7 +71,13 @@ hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids,
                         int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);
 hipError_t launch_gateup(const SweepParams& p, int rows, int max_slots, hipStream_t s);
 hipError_t launch_down(const SweepParams& p, int rows, int max_union, hipStream_t s);
+// out = bf16(sum_j w*y + gamma*s); with partial non-null, partial = sum_j w*y
+// (fp32, slots mapped to -1 skipped) and out is not written.
 hipError_t launch_blend(const float* y, const float* w, const int32_t* slot_to_union, const float* gamma,
-                        uint16_t* out, int rows, int h, int k, hipStream_t s);
+                        uint16_t* out, float* partial, int rows, int h, int k, hipStream_t s);
+hipError_t launch_union_local(const int32_t* ids, int rows, int k, int lo, int hi, int32_t* union_ids,
+                              int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);
+hipError_t launch_ep_combine(const float* reduced, const float* y, const float* gamma, uint16_t* out, int rows, int h,
+                             hipStream_t s);
 
 }  // namespace moe

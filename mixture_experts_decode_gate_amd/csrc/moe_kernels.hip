@@ -44,17 +44,21 @@ constexpr int kMaxRouterChunks = MOE_MAX_DIM / kRouterChunk;
 constexpr int kRouteThreads = 64 * (kMaxRouterChunks > kMaxRows ? kMaxRouterChunks : kMaxRows);
 static_assert(MOE_MAX_EXPERTS <= 64 * 16, "top-k holds at most 16 keys per lane");
 
-// Union of the n <= 64 ids in ids_lds (slot t = r*k + j).  Lane t compares its
-// id with every slot at once (broadcast LDS reads, no sort): slot t is a first
-// occurrence when no earlier slot holds its id.  First occurrences, in slot
-// order, form the union.  Returns the lane's union position if it is a first
+// Union of the n <= 64 ids in ids_lds (slot t = r*k + j) that lie in
+// [lo, hi).  Lane t compares its id with every slot at once (broadcast LDS
+// reads, no sort): slot t is a first occurrence when its id is in range and no
+// earlier slot holds it.  First occurrences, in slot order, form the union;
+// a slot whose id is out of range maps to -1 (under expert parallelism
+// forward_ep.rs splits the selected ids into local and remote ones by
+// local_expert_range).  Returns the lane's union position if it is a first
 // occurrence (else -1), in *mask_out the rows that chose its id and in
 // *count_out the union size U.  The union outputs are written when
 // union_ids is not null (row_mask may be null on its own).
-__device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows, int lane, int32_t* union_ids,
-                          int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask, uint32_t* mask_out,
-                          int* count_out) {
+__device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows, int lo, int hi, int lane,
+                          int32_t* union_ids, int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask,
+                          uint32_t* mask_out, int* count_out) {
   const int id = lane < n ? ids_lds[lane] : -1;
+  const bool local = id >= lo && id < hi;
   uint64_t eq = 0;
 #pragma unroll
   for (int t4 = 0; t4 < kMaxIds / 4; ++t4) {
@@ -70,12 +74,12 @@ __device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows, int la
   const uint64_t kmask = k >= 64 ? ~0ull : ((1ull << k) - 1ull);
   for (int r = 0; r < rows; ++r)
     if ((eq >> (r * k)) & kmask) mask |= 1u << r;
-  const bool is_first = (lane < n) && (first == lane);
+  const bool is_first = (lane < n) && local && (first == lane);
   const unsigned long long bal = __ballot(is_first);
   const int pos_self = __popcll(bal & ((1ull << lane) - 1ull));
   const int pos_first = __popcll(bal & ((1ull << first) - 1ull));
   if (union_ids != nullptr) {
-    if (lane < n) slot_to_union[lane] = pos_first;
+    if (lane < n) slot_to_union[lane] = local ? pos_first : -1;
     if (is_first) {
       union_ids[pos_self] = id;
       if (row_mask) row_mask[pos_self] = mask;
@@ -107,7 +111,7 @@ __device__ int identity_slots(const int32_t* ids_lds, int n, int k, int lane, in
   return used ? lane : -1;
 }
 
-__global__ __launch_bounds__(64) void union_kernel(const int32_t* __restrict__ ids, int rows, int k,
+__global__ __launch_bounds__(64) void union_kernel(const int32_t* __restrict__ ids, int rows, int k, int lo, int hi,
                                                    int32_t* union_ids, int32_t* union_count,
                                                    int32_t* slot_to_union, uint32_t* row_mask) {
   __shared__ __align__(16) int32_t s_ids[kMaxIds];
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(64) void union_kernel(const int32_t* __restrict__ i
   __syncthreads();
   uint32_t mask;
   int count;
-  union_wave(s_ids, n, k, rows, lane, union_ids, union_count, slot_to_union, row_mask, &mask, &count);
+  union_wave(s_ids, n, k, rows, lo, hi, lane, union_ids, union_count, slot_to_union, row_mask, &mask, &count);
 }
 
 // Order-preserving map of a float key to uint32 (larger float -> larger
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int
       // The gate takes the fp64 sum; routing scores take the fp32 logit, the
       // value top-k sees.
       if (e == E)
-        sg = 1.0 / (1.0 + exp(-z));
+        sg = p.ungated ? 1.0 : 1.0 / (1.0 + exp(-z));
       else if (p.route_kind == MOE_ROUTE_SIGMOID_BIAS)
         sg = 1.0 / (1.0 + exp(-(double)(float)z));
     }
@@ -689,7 +693,8 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     int count;
     const int pos = p.token_major
                         ? identity_slots(s_ids, R * rp.k, rp.k, lane, s_uids, &s_union, s_s2u, s_rmask, &mask, &count)
-                        : union_wave(s_ids, R * rp.k, rp.k, R, lane, s_uids, &s_union, s_s2u, s_rmask, &mask, &count);
+                        : union_wave(s_ids, R * rp.k, rp.k, R, rp.expert_lo, rp.expert_hi, lane, s_uids, &s_union,
+                                     s_s2u, s_rmask, &mask, &count);
     if (pos >= 0) {  // lane is the union entry's first slot
       const int ex = s_ids[lane];
       s_slots[pos] = slot_info(kPtab ? s_ptab[ex] : expert_ptrs(rp, ex), ex, rp.inter, mask);
@@ -1016,20 +1021,43 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
 
 // Weighted sum and shared-expert blend, one thread per (row, column):
 //   out[r][n] = bf16( sum_{j<k} w[r][j] * y[slot(r,j)][r][n] + gamma[r] * y[shared][r][n] )
-// summed in fp32 in ascending j.
+// summed in fp32 in ascending j.  With partial non-null (one rank's share
+// under expert parallelism) it writes the routed sum alone, in fp32, over the
+// slots whose expert is local (slot_to_union >= 0): forward_token_major.rs
+// blends with a zeroed shared term before the all-reduce.
 __global__ __launch_bounds__(256) void blend_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                     const int32_t* __restrict__ slot_to_union,
                                                     const float* __restrict__ gamma, uint16_t* __restrict__ out,
-                                                    int h, int k) {
+                                                    float* __restrict__ partial, int h, int k) {
   const int r = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= h) return;
   float acc = 0.f;
   for (int j = 0; j < k; ++j) {
     const int s = slot_to_union[r * k + j];
-    acc = __builtin_fmaf(w[r * k + j], y[((size_t)s * kMaxRows + r) * h + n], acc);
+    if (s >= 0) acc = __builtin_fmaf(w[r * k + j], y[((size_t)s * kMaxRows + r) * h + n], acc);
+  }
+  if (partial != nullptr) {
+    partial[(size_t)r * h + n] = acc;
+    return;
   }
   acc = __builtin_fmaf(gamma[r], y[((size_t)kSharedSlot * kMaxRows + r) * h + n], acc);
+  out[(size_t)r * h + n] = f32_to_bf16(acc);
+}
+
+// The shared expert added after the all-reduce of the ranks' partials
+// (forward_token_major.rs: moe_batched_blend, or residual_add when the gate
+// weight is null, where gamma = 1):
+//   out[r][n] = bf16( reduced[r][n] + gamma[r] * y[shared][r][n] )
+__global__ __launch_bounds__(256) void ep_combine_kernel(const float* __restrict__ reduced,
+                                                         const float* __restrict__ y,
+                                                         const float* __restrict__ gamma,
+                                                         uint16_t* __restrict__ out, int h) {
+  const int r = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= h) return;
+  const float acc =
+      __builtin_fmaf(gamma[r], y[((size_t)kSharedSlot * kMaxRows + r) * h + n], reduced[(size_t)r * h + n]);
   out[(size_t)r * h + n] = f32_to_bf16(acc);
 }
 
@@ -1174,7 +1202,14 @@ hipError_t launch_route(const RouteParams& p, bool do_topk, hipStream_t s) {
 
 hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids, int32_t* union_count,
                         int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s) {
-  hipLaunchKernelGGL(union_kernel, dim3(1), dim3(64), 0, s, ids, rows, k, union_ids, union_count,
+  hipLaunchKernelGGL(union_kernel, dim3(1), dim3(64), 0, s, ids, rows, k, 0, MOE_MAX_EXPERTS, union_ids,
+                     union_count, slot_to_union, row_mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_union_local(const int32_t* ids, int rows, int k, int lo, int hi, int32_t* union_ids,
+                              int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s) {
+  hipLaunchKernelGGL(union_kernel, dim3(1), dim3(64), 0, s, ids, rows, k, lo, hi, union_ids, union_count,
                      slot_to_union, row_mask);
   return hipGetLastError();
 }
@@ -1213,9 +1248,16 @@ hipError_t launch_down(const SweepParams& p, int rows, int max_union, hipStream_
 }
 
 hipError_t launch_blend(const float* y, const float* w, const int32_t* slot_to_union, const float* gamma,
-                        uint16_t* out, int rows, int h, int k, hipStream_t s) {
+                        uint16_t* out, float* partial, int rows, int h, int k, hipStream_t s) {
   dim3 grid((h + 255) / 256, rows);
-  hipLaunchKernelGGL(blend_kernel, grid, dim3(256), 0, s, y, w, slot_to_union, gamma, out, h, k);
+  hipLaunchKernelGGL(blend_kernel, grid, dim3(256), 0, s, y, w, slot_to_union, gamma, out, partial, h, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_ep_combine(const float* reduced, const float* y, const float* gamma, uint16_t* out, int rows, int h,
+                             hipStream_t s) {
+  dim3 grid((h + 255) / 256, rows);
+  hipLaunchKernelGGL(ep_combine_kernel, grid, dim3(256), 0, s, reduced, y, gamma, out, h);
   return hipGetLastError();
 }
 

@@ -22,12 +22,12 @@ def _torch():
 
 
 class DeviceLayer:
-    """router_w [E, h] fp32, bias [E] fp32 or None, shared_gate_vec [h] fp32,
+    """router_w [E, h] fp32, bias [E] fp32 or None, shared_gate_vec [h] fp32 or None (ungated),
     shared = (gate, up, down) NVFP4 objects (n, k, packed, scales, scale2),
     expert(e, p) -> NVFP4 object of routed expert e, projection p (0 gate, 1 up, 2 down)."""
 
     def __init__(self, cfg: MoeConfig, router_w: np.ndarray, bias: Optional[np.ndarray],
-                 shared_gate_vec: np.ndarray, shared: Sequence, expert: Callable[[int, int], object],
+                 shared_gate_vec: Optional[np.ndarray], shared: Sequence, expert: Callable[[int, int], object],
                  device: str = "cuda"):
         torch = _torch()
         self.cfg = cfg
@@ -36,7 +36,8 @@ class DeviceLayer:
         dev = torch.device(device)
         self.router_w = torch.from_numpy(np.ascontiguousarray(router_w, np.float32)).to(dev)
         self.bias = None if bias is None else torch.from_numpy(np.ascontiguousarray(bias, np.float32)).to(dev)
-        self.shared_gate_vec = torch.from_numpy(np.ascontiguousarray(shared_gate_vec, np.float32)).to(dev)
+        self.shared_gate_vec = None if shared_gate_vec is None else torch.from_numpy(
+            np.ascontiguousarray(shared_gate_vec, np.float32)).to(dev)
         self.shared = []
         for t in shared:
             self.shared.append((torch.from_numpy(np.ascontiguousarray(t.packed)).to(dev),
@@ -77,7 +78,7 @@ class DeviceLayer:
                                             self.scale2[p].data_ptr()))
         for name, (pk, sc, s2) in zip(("shared_gate", "shared_up", "shared_down"), self.shared):
             setattr(w, name, MoeNvfp4(pk.data_ptr(), sc.data_ptr(), s2))
-        w.shared_expert_gate = self.shared_gate_vec.data_ptr()
+        w.shared_expert_gate = 0 if self.shared_gate_vec is None else self.shared_gate_vec.data_ptr()
         return w
 
     def clone(self) -> "DeviceLayer":
@@ -86,7 +87,7 @@ class DeviceLayer:
         new.cfg, new.device = self.cfg, self.device
         new.router_w = self.router_w.clone()
         new.bias = None if self.bias is None else self.bias.clone()
-        new.shared_gate_vec = self.shared_gate_vec.clone()
+        new.shared_gate_vec = None if self.shared_gate_vec is None else self.shared_gate_vec.clone()
         new.shared = [(pk.clone(), sc.clone(), s2) for pk, sc, s2 in self.shared]
         new.packed = [t.clone() for t in self.packed]
         new.scales = [t.clone() for t in self.scales]
@@ -95,7 +96,7 @@ class DeviceLayer:
         return new
 
     def nbytes(self) -> int:
-        n = self.router_w.numel() * 4 + self.shared_gate_vec.numel() * 4
+        n = self.router_w.numel() * 4 + (0 if self.shared_gate_vec is None else self.shared_gate_vec.numel() * 4)
         n += 0 if self.bias is None else self.bias.numel() * 4
         n += sum(pk.numel() + sc.numel() for pk, sc, _ in self.shared)
         n += sum(t.numel() for t in self.packed) + sum(t.numel() for t in self.scales)

@@ -131,8 +131,8 @@ def test_unsupported_layers():
     w.shared_up = moe.MoeNvfp4(0, 0, 1.0)          # no shared expert
     assert forward(cfg_c4(), w) == moe.MOE_ERR_UNSUPPORTED
     w = fake_weights()
-    w.shared_expert_gate = 0                       # ungated shared expert
-    assert forward(cfg_c4(), w) == moe.MOE_ERR_UNSUPPORTED
+    w.shared_expert_gate = BASE + 0x3008           # misaligned gate vector
+    assert forward(cfg_c4(), w) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_small_workspace_refused():
@@ -195,3 +195,34 @@ def test_token_major_refuses_like_forward():
     cfg = cfg_c4()
     need = lib.moe_workspace_bytes(ctypes.byref(cfg))
     assert both(cfg, fake_weights(), ws_bytes=need - 1) == (moe.MOE_ERR_WORKSPACE, moe.MOE_ERR_WORKSPACE)
+
+
+def test_ep_refusals():
+    cfg = cfg_c4()
+    need = lib.moe_workspace_bytes(ctypes.byref(cfg))
+    P = BASE + 0x40000000
+
+    def ep(lo, hi, partial=P, rows=4, x=X):
+        return lib.moe_forward_ep_partial(ctypes.byref(cfg), ctypes.byref(fake_weights()), x, partial, rows, lo, hi,
+                                          WS, need, None)
+    for lo, hi in [(-1, 8), (9, 8), (0, 257), (0, -1)]:
+        assert ep(lo, hi) == moe.MOE_ERR_INVALID_ARG, (lo, hi)
+    assert ep(0, 32, partial=0) == moe.MOE_ERR_INVALID_ARG
+    assert ep(0, 32, partial=P + 4) == moe.MOE_ERR_INVALID_ARG         # misaligned
+    assert ep(0, 32, partial=X + 256) == moe.MOE_ERR_INVALID_ARG       # overlaps x
+    assert ep(0, 32, partial=WS + 4096) == moe.MOE_ERR_INVALID_ARG     # inside the workspace
+    assert ep(0, 32, rows=9) == moe.MOE_ERR_INVALID_ARG
+
+    def comb(red, out, rows=4, ws_bytes=need):
+        return lib.moe_ep_combine(ctypes.byref(cfg), red, out, rows, WS, ws_bytes, None)
+    assert comb(0, OUT) == moe.MOE_ERR_INVALID_ARG
+    assert comb(P, 0) == moe.MOE_ERR_INVALID_ARG
+    assert comb(P, P + 1024) == moe.MOE_ERR_INVALID_ARG                # out overlaps reduced
+    assert comb(P, OUT, rows=0) == moe.MOE_ERR_INVALID_ARG
+    assert comb(P, OUT, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+
+    u = lambda lo, hi, E=256: lib.moe_union_local(X, 2, 8, E, lo, hi, OUT, OUT + 512, OUT + 1024, OUT + 2048, None)
+    for lo, hi in [(-1, 4), (5, 4), (0, 300)]:
+        assert u(lo, hi) == moe.MOE_ERR_INVALID_ARG, (lo, hi)
+    assert lib.moe_union_local(X, 9, 8, 256, 0, 8, OUT, OUT + 512, OUT + 1024, OUT + 2048, None) == \
+        moe.MOE_ERR_INVALID_ARG

@@ -290,3 +290,138 @@ def test_token_major_256(layer256):
     for name in ("c3_e256_verify4", "c4_e256_prefill8"):
         shape = synth.CONFIGS[name]
         check_token_major(dl, synth.activations(shape, 2))
+
+
+# ---------------------------------------------------------------- expert-parallel share and ungated shared expert
+from oracle.layer import ep_combine, routed_partial_row  # noqa: E402
+from oracle.union import expert_union_local  # noqa: E402
+
+
+def test_union_local_matches_oracle():
+    torch = torch_cuda()
+    moe = moe_mod()
+    rng = np.random.default_rng(31)
+    for _ in range(60):
+        E = int(rng.integers(4, 300))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        R = min(8, int(rng.integers(1, 64 // k + 1)))
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(R)]).astype(np.int32)
+        lo = int(rng.integers(0, E + 1))
+        hi = int(rng.integers(lo, E + 1))
+        d_ids = torch.from_numpy(ids).cuda()
+        uid = torch.full((64,), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+        s2u = torch.full((R * k,), -7, dtype=torch.int32, device="cuda")
+        msk = torch.zeros(64, dtype=torch.int32, device="cuda")
+        moe.moe_union_local(d_ids, lo, hi, uid, cnt, s2u, msk, num_experts=E)
+        torch.cuda.synchronize()
+        u, U, ls2u, lmask = expert_union_local(ids, lo, hi)
+        assert int(cnt.item()) == U
+        assert np.array_equal(uid.cpu().numpy()[:U], u)
+        assert np.array_equal(s2u.cpu().numpy(), ls2u)
+        assert np.array_equal(msk.cpu().numpy().view(np.uint32)[:U], lmask)
+
+
+def run_ep_partial(dl, x_bits, lo, hi):
+    torch = torch_cuda()
+    moe = moe_mod()
+    x = x_dev(x_bits)
+    R, h = x_bits.shape
+    partial = torch.full((R, h), float("nan"), dtype=torch.float32, device="cuda")
+    ws = ws_for(dl.cfg)
+    moe.moe_forward_ep_partial(dl.cfg, dl.weights, x, partial, lo, hi, ws)
+    torch.cuda.synchronize()
+    return partial.cpu().numpy(), ws
+
+
+def run_ep_combine(dl, reduced, ws):
+    torch = torch_cuda()
+    moe = moe_mod()
+    red = torch.from_numpy(np.ascontiguousarray(reduced, np.float32)).cuda()
+    out = torch.zeros(reduced.shape, dtype=torch.int16, device="cuda")
+    moe.moe_ep_combine(dl.cfg, red, out, ws)
+    torch.cuda.synchronize()
+    return out_bits(out)
+
+
+def check_ep_shares(weights, dl, x_bits, ranges, rows_checked=None):
+    """Each rank's local union exactly, its partial against the oracle's (rows
+    without a local expert exactly zero), then the combine of the reduced
+    partials against the oracle's output.  The reduce across ranks is done here
+    on the host, in float64 in rank order: it stands in for the all-reduce,
+    which is not part of the library."""
+    R, k = x_bits.shape[0], dl.cfg.top_k
+    ref = moe_layer_from(weights, x_bits, rows=rows_checked)
+    rows = ref["rows"]
+    reduced = np.zeros((R, dl.cfg.hidden), np.float64)
+    ws = None
+    for lo, hi in ranges:
+        part, ws = run_ep_partial(dl, x_bits, lo, hi)
+        mid = read_intermediates(dl, ws, R)
+        u, U, s2u, mask = expert_union_local(ref["ids"], lo, hi)
+        assert mid["union_count"] == U, (lo, hi)
+        assert np.array_equal(mid["union_ids"], u)
+        assert np.array_equal(mid["slot_to_union"], s2u)
+        assert np.array_equal(mid["row_mask"], mask)
+        for r in rows:
+            local = (ref["ids"][r] >= lo) & (ref["ids"][r] < hi)
+            want = routed_partial_row(ref["weights"][r], ref["y"][r], local).astype(np.float64)
+            got = part[r].astype(np.float64)
+            if not local.any():
+                assert np.all(got == 0.0), (lo, hi, r)
+            else:
+                assert np.linalg.norm(got - want) <= REL_L2_TOL * np.linalg.norm(want), (lo, hi, r)
+        reduced += part.astype(np.float64)
+    out = run_ep_combine(dl, reduced.astype(np.float32), ws)
+    rel_l2, rel_max = output_errors(out[rows], ref["out"][rows])
+    assert np.all(rel_l2 <= REL_L2_TOL) and np.all(rel_max <= REL_MAX_TOL), (rel_l2, rel_max)
+    want_comb = ep_combine(reduced.astype(np.float32), ref["gamma"], ref["shared_y"])
+    rel_l2, _ = output_errors(out[rows], want_comb[rows])
+    assert np.all(rel_l2 <= REL_L2_TOL), rel_l2
+    return out
+
+
+@pytest.mark.parametrize("name", ["c0_tiny", "c2_e128_verify2"])
+def test_ep_shares_small_configs(name):
+    shape = synth.CONFIGS[name]
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = synth.activations(shape, 0)
+    E = shape.num_experts
+    ranges = [(0, E // 4), (E // 4, E // 2), (E // 2, E // 2), (E // 2, 3 * E // 4), (3 * E // 4, E)]
+    check_ep_shares(weights, dl, x, ranges)
+
+
+@pytest.mark.parametrize("shape", [s for s in RAGGED if s.name in ("ragged_h", "ids64")], ids=lambda s: s.name)
+def test_ep_full_range_equals_forward(shape):
+    # With every expert local, the partial plus the combine is the same fp32
+    # chain moe_forward's blend runs: the bytes must be identical.
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = synth.activations(shape, 1)
+    want, _ = run_forward(dl, x)
+    part, ws = run_ep_partial(dl, x, 0, shape.num_experts)
+    assert np.array_equal(run_ep_combine(dl, part, ws), want)
+    check_ep_shares(weights, dl, x, [(0, 5), (5, shape.num_experts)])
+
+
+def test_ep_shares_256(layer256):
+    weights, dl = layer256
+    shape = synth.CONFIGS["c4_e256_prefill8"]
+    x = synth.activations(shape, 0)
+    ranges = [(32 * g, 32 * (g + 1)) for g in range(8)]
+    check_ep_shares(weights, dl, x, ranges, rows_checked=[0, 7])
+
+
+@pytest.mark.parametrize("name", ["c0_tiny", "c2_e128_verify2"])
+def test_ungated_shared_expert(name):
+    shape = synth.CONFIGS[name]
+    weights = synth.layer_weights(shape)
+    weights.shared_gate_vec = None
+    dl = upload(weights)
+    x = synth.activations(shape, 0)
+    check_against_oracle(weights, dl, x)
+    _, ws = run_forward(dl, x)
+    assert np.all(read_intermediates(dl, ws, shape.rows)["gamma"] == 1.0)
+    check_token_major(dl, x)
+    check_ep_shares(weights, dl, x, [(0, shape.num_experts // 2), (shape.num_experts // 2, shape.num_experts)])
