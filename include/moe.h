@@ -26,7 +26,8 @@
  *   SHARED-expert note: the shared expert runs once over all rows.
  *
  * Per row r:
- *   L[r,e]   = sum_t x[r,t] * router_w[e,t]                     (fp32 result)
+ *   L[r,e]   = sum_t x[r,t] * router_w[e,t]                     (fp32 result;
+ *              router_w dense fp32, or the NVFP4 router_nvfp4 decoded exactly)
  *   softmax: ids = top_k of L[r,:]; w = softmax weights of those ids,
  *            renormalised over the k ids when norm_topk_prob.
  *   sigmoid: s = sigmoid(L); ids = top_k of fp32(s + bias);
@@ -121,7 +122,7 @@ typedef struct moe_expert_table {
 } moe_expert_table;
 
 typedef struct moe_weights {
-  const float* router_w;           /* [E, h] fp32, row-major                    */
+  const float* router_w;           /* [E, h] fp32, row-major; NULL: router_nvfp4 */
   const float* correction_bias;    /* [E] fp32 for SIGMOID_BIAS, NULL otherwise  */
   moe_expert_table gate;           /* [I, h] per expert                          */
   moe_expert_table up;             /* [I, h] per expert                          */
@@ -133,6 +134,12 @@ typedef struct moe_weights {
                                       the shared expert is added ungated (gate 1),
                                       as forward_token_major.rs does with
                                       residual_add when the gate weight is null */
+  moe_nvfp4 router_nvfp4;          /* [E, h] NVFP4 router, used when router_w is
+                                      NULL (forward_ep.rs and
+                                      forward_token_major.rs run the gate
+                                      projection as an NVFP4 GEMV / GEMM); its
+                                      packed and scales must be NULL when
+                                      router_w is set */
 } moe_weights;
 
 /* Byte offsets of the intermediates moe_forward leaves in the workspace.

@@ -69,7 +69,7 @@ class MoeWeights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("correction_bias", ctypes.c_void_p),
                 ("gate", MoeExpertTable), ("up", MoeExpertTable), ("down", MoeExpertTable),
                 ("shared_gate", MoeNvfp4), ("shared_up", MoeNvfp4), ("shared_down", MoeNvfp4),
-                ("shared_expert_gate", ctypes.c_void_p)]
+                ("shared_expert_gate", ctypes.c_void_p), ("router_nvfp4", MoeNvfp4)]
 
 
 class MoeWsLayout(ctypes.Structure):

@@ -97,8 +97,18 @@ moe_status check_table(const moe_expert_table& t, const char* name) {
 
 moe_status check_route_weights(const moe_config* c, const moe_weights* w) {
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
-  if (!w->router_w || !aligned(w->router_w, 16))
-    return fail(MOE_ERR_INVALID_ARG, "router_w must be a 16-byte aligned device pointer");
+  if (w->router_w) {
+    if (!aligned(w->router_w, 16)) return fail(MOE_ERR_INVALID_ARG, "router_w must be 16-byte aligned");
+    if (w->router_nvfp4.packed || w->router_nvfp4.scales)
+      return fail(MOE_ERR_INVALID_ARG, "router_w and router_nvfp4 are both set");
+  } else {
+    const moe_nvfp4& r = w->router_nvfp4;
+    if (!r.packed || !r.scales) return fail(MOE_ERR_INVALID_ARG, "no router: router_w and router_nvfp4 are NULL");
+    if (!aligned(r.packed, 16) || !aligned(r.scales, 16))
+      return fail(MOE_ERR_INVALID_ARG, "router_nvfp4 packed and scales must be 16-byte aligned");
+    const float s2 = r.scale2;
+    if (!(s2 == s2) || s2 > 3.0e38f || s2 < -3.0e38f) return fail(MOE_ERR_INVALID_ARG, "router scale2 is not finite");
+  }
   if (c->route_kind == MOE_ROUTE_SIGMOID_BIAS) {
     if (!w->correction_bias || !aligned(w->correction_bias, 4))
       return fail(MOE_ERR_INVALID_ARG, "sigmoid routing needs an aligned correction_bias");
@@ -206,16 +216,20 @@ void fill_route(moe::RouteParams& p, const moe_config* c, const moe_weights* w, 
   memset(&p, 0, sizeof p);
   p.x = x;
   p.router_w = w->router_w;
-  // Without a gate vector the gate pass reads the router's first row (any h
-  // readable floats) and writes gamma = 1.
-  p.gate_vec = w->shared_expert_gate ? w->shared_expert_gate : w->router_w;
+  p.router_fp4 = w->router_w ? 0 : 1;
+  p.router_packed = w->router_nvfp4.packed;
+  p.router_scales = w->router_nvfp4.scales;
+  p.router_scale2 = w->router_nvfp4.scale2;
+  // Without a gate vector the gate pass reads the workspace's expert outputs
+  // (any h readable floats; written later in the call) and writes gamma = 1.
+  p.gate_vec = w->shared_expert_gate ? w->shared_expert_gate : reinterpret_cast<const float*>(ws + L.y);
   p.ungated = w->shared_expert_gate ? 0 : 1;
   p.expert_lo = 0;
   p.expert_hi = c->num_experts;
   p.h = c->hidden;
   // Top-k reads bias[e] unconditionally; softmax routing ignores the value,
-  // so it reads the router weights (at least E floats) there instead.
-  p.bias = w->correction_bias ? w->correction_bias : w->router_w;
+  // so it reads the workspace's expert outputs (at least E floats) instead.
+  p.bias = w->correction_bias ? w->correction_bias : reinterpret_cast<const float*>(ws + L.y);
   p.E = c->num_experts;
   p.k = c->top_k;
   p.rows = rows;

@@ -21,7 +21,11 @@ constexpr int kSegCostBase = 3;
 
 struct RouteParams {
   const uint16_t* x;       // [rows][h] bf16
-  const float* router_w;   // [E][h]
+  const float* router_w;   // [E][h] fp32 (dense router), or null with router_fp4
+  const uint8_t* router_packed;  // NVFP4 router [E][h/2] codes (router_fp4)
+  const uint8_t* router_scales;  // NVFP4 router [E][h/16] E4M3 block scales
+  float router_scale2;
+  int router_fp4;
   const float* gate_vec;   // [h] shared-expert gate vector
   int h;
   const float* bias;       // [E]; for softmax any readable [E] floats (ignored)

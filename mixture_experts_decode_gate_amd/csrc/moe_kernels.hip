@@ -256,6 +256,82 @@ __device__ void topk_select(const RouteParams& p, int r, int lane, TopkIn<G>& in
   }
 }
 
+// This lane's share of chunk c of one dense fp32 router row (or the gate
+// vector) times the R input rows, in fp64: bf16 x fp32 products are exact in
+// fp64.  Lanes past h load an in-bounds copy and add zeros.
+template <int R>
+__device__ __forceinline__ void router_dot_f32(const RouteParams& p, const float* row, int c, int lane,
+                                               double (&acc)[R]) {
+  const int h = p.h;
+  constexpr int kIt = kRouterChunk / 256;
+  float4 wv[kIt];
+  uint2 xv[R][kIt];
+  bool ok[kIt];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int col = c * kRouterChunk + it * 256 + lane * 4;
+    ok[it] = col < h;
+    const int cc = ok[it] ? col : h - 4;  // in-bounds; the contribution is dropped below
+    const u32x4 w4 = ld_stream(reinterpret_cast<const uint8_t*>(row + cc));
+    wv[it] = make_float4(__uint_as_float(w4.x), __uint_as_float(w4.y), __uint_as_float(w4.z), __uint_as_float(w4.w));
+#pragma unroll
+    for (int r = 0; r < R; ++r) xv[r][it] = *reinterpret_cast<const uint2*>(p.x + (size_t)r * h + cc);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    acc[r] = 0.0;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const double w0 = ok[it] ? (double)wv[it].x : 0.0, w1 = ok[it] ? (double)wv[it].y : 0.0;
+      const double w2 = ok[it] ? (double)wv[it].z : 0.0, w3 = ok[it] ? (double)wv[it].w : 0.0;
+      acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].x & 0xFFFFu), w0, acc[r]);
+      acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].x >> 16), w1, acc[r]);
+      acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].y & 0xFFFFu), w2, acc[r]);
+      acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].y >> 16), w3, acc[r]);
+    }
+  }
+}
+
+// The same for an NVFP4 router row e: lane covers 8 consecutive columns (4
+// bytes of E2M1 codes, even column in the low nibble, and their E4M3 block
+// scale).  code x scale is exact in fp32 (at most 6 significant bits) and its
+// product with a bf16 input exact in fp64; the per-tensor scale2 multiplies
+// the row's finished fp64 sum.  Lanes past h load an in-bounds copy and take
+// a zero scale.
+template <int R>
+__device__ __forceinline__ void router_dot_nvfp4(const RouteParams& p, int e, int c, int lane, double (&acc)[R]) {
+  typedef __attribute__((address_space(1))) const uint32_t global_u32;
+  typedef __attribute__((address_space(1))) const uint8_t global_u8;
+  const int h = p.h;
+  const int col = c * kRouterChunk + lane * 8;
+  const bool ok = col < h;
+  const int cc = ok ? col : h - 8;
+  const uint32_t q = __builtin_nontemporal_load((global_u32*)(p.router_packed + (size_t)e * (size_t)(h >> 1) + (cc >> 1)));
+  const uint32_t sb = __builtin_nontemporal_load((global_u8*)(p.router_scales + (size_t)e * (size_t)(h >> 4) + (cc >> 4)));
+  u32x4 xv[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) xv[r] = *reinterpret_cast<const u32x4*>(p.x + (size_t)r * h + cc);
+  const double sc = ok ? (double)e4m3<0>(sb) : 0.0;
+  double wv[8];
+  const bf16x2 d0 = e2m1x2<0>(q), d1 = e2m1x2<1>(q), d2 = e2m1x2<2>(q), d3 = e2m1x2<3>(q);
+  const uint32_t du[4] = {__builtin_bit_cast(uint32_t, d0), __builtin_bit_cast(uint32_t, d1),
+                          __builtin_bit_cast(uint32_t, d2), __builtin_bit_cast(uint32_t, d3)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wv[2 * i] = (double)bf16_to_f32(du[i] & 0xFFFFu) * sc;
+    wv[2 * i + 1] = (double)bf16_to_f32(du[i] >> 16) * sc;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    acc[r] = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][i] & 0xFFFFu), wv[2 * i], acc[r]);
+      acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][i] >> 16), wv[2 * i + 1], acc[r]);
+    }
+  }
+}
+
 template <int R, int G>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int do_topk) {
   __shared__ double part[kMaxRouterChunks][kMaxRows];
@@ -269,35 +345,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int
 
   if (wave < nkc) {
     const int c = wave;
-    const float* row = (e < E) ? p.router_w + (size_t)e * h : p.gate_vec;
-    constexpr int kIt = kRouterChunk / 256;
-    float4 wv[kIt];
-    uint2 xv[R][kIt];
-    bool ok[kIt];
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int col = c * kRouterChunk + it * 256 + lane * 4;
-      ok[it] = col < h;
-      const int cc = ok[it] ? col : h - 4;  // in-bounds; the contribution is dropped below
-      const u32x4 w4 = ld_stream(reinterpret_cast<const uint8_t*>(row + cc));
-      wv[it] = make_float4(__uint_as_float(w4.x), __uint_as_float(w4.y), __uint_as_float(w4.z), __uint_as_float(w4.w));
-#pragma unroll
-      for (int r = 0; r < R; ++r) xv[r][it] = *reinterpret_cast<const uint2*>(p.x + (size_t)r * h + cc);
-    }
     double acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      acc[r] = 0.0;
-#pragma unroll
-      for (int it = 0; it < kIt; ++it) {
-        const double w0 = ok[it] ? (double)wv[it].x : 0.0, w1 = ok[it] ? (double)wv[it].y : 0.0;
-        const double w2 = ok[it] ? (double)wv[it].z : 0.0, w3 = ok[it] ? (double)wv[it].w : 0.0;
-        acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].x & 0xFFFFu), w0, acc[r]);
-        acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].x >> 16), w1, acc[r]);
-        acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].y & 0xFFFFu), w2, acc[r]);
-        acc[r] = __builtin_fma((double)bf16_to_f32(xv[r][it].y >> 16), w3, acc[r]);
-      }
-    }
+    if (p.router_fp4 && e < E)
+      router_dot_nvfp4<R>(p, e, c, lane, acc);
+    else
+      router_dot_f32<R>(p, (e < E) ? p.router_w + (size_t)e * h : p.gate_vec, c, lane, acc);
     wave_sum_n<R>(acc);
     if (lane == 0) {
 #pragma unroll
@@ -317,6 +369,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int
     double z = 0.0, sg = 0.0;
     if (lane < R) {
       for (int cc = 0; cc < nkc; ++cc) z += part[cc][lane];
+      if (p.router_fp4 && e < E) z *= (double)p.router_scale2;
       // The gate takes the fp64 sum; routing scores take the fp32 logit, the
       // value top-k sees.
       if (e == E)

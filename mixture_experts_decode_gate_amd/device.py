@@ -22,7 +22,7 @@ def _torch():
 
 
 class DeviceLayer:
-    """router_w [E, h] fp32, bias [E] fp32 or None, shared_gate_vec [h] fp32 or None (ungated),
+    """router_w [E, h] fp32 or an NVFP4 object [E, h], bias [E] fp32 or None, shared_gate_vec [h] fp32 or None (ungated),
     shared = (gate, up, down) NVFP4 objects (n, k, packed, scales, scale2),
     expert(e, p) -> NVFP4 object of routed expert e, projection p (0 gate, 1 up, 2 down)."""
 
@@ -34,7 +34,14 @@ class DeviceLayer:
         self.device = device
         E, h, I = cfg.num_experts, cfg.hidden, cfg.moe_inter
         dev = torch.device(device)
-        self.router_w = torch.from_numpy(np.ascontiguousarray(router_w, np.float32)).to(dev)
+        if hasattr(router_w, "packed"):  # NVFP4 router [E, h]
+            self.router_w = None
+            self.router_nvfp4 = (torch.from_numpy(np.ascontiguousarray(router_w.packed)).to(dev),
+                                 torch.from_numpy(np.ascontiguousarray(router_w.scales)).to(dev),
+                                 float(router_w.scale2))
+        else:
+            self.router_w = torch.from_numpy(np.ascontiguousarray(router_w, np.float32)).to(dev)
+            self.router_nvfp4 = None
         self.bias = None if bias is None else torch.from_numpy(np.ascontiguousarray(bias, np.float32)).to(dev)
         self.shared_gate_vec = None if shared_gate_vec is None else torch.from_numpy(
             np.ascontiguousarray(shared_gate_vec, np.float32)).to(dev)
@@ -71,7 +78,12 @@ class DeviceLayer:
 
     def _weights(self) -> MoeWeights:
         w = MoeWeights()
-        w.router_w = self.router_w.data_ptr()
+        if self.router_w is not None:
+            w.router_w = self.router_w.data_ptr()
+        else:
+            pk, sc, s2 = self.router_nvfp4
+            w.router_w = 0
+            w.router_nvfp4 = MoeNvfp4(pk.data_ptr(), sc.data_ptr(), s2)
         w.correction_bias = 0 if self.bias is None else self.bias.data_ptr()
         for name, p in (("gate", 0), ("up", 1), ("down", 2)):
             setattr(w, name, MoeExpertTable(self.tables[p][0].data_ptr(), self.tables[p][1].data_ptr(),
@@ -85,7 +97,9 @@ class DeviceLayer:
         """A copy of every tensor at new device addresses (same values)."""
         new = object.__new__(DeviceLayer)
         new.cfg, new.device = self.cfg, self.device
-        new.router_w = self.router_w.clone()
+        new.router_w = None if self.router_w is None else self.router_w.clone()
+        new.router_nvfp4 = None if self.router_nvfp4 is None else (
+            self.router_nvfp4[0].clone(), self.router_nvfp4[1].clone(), self.router_nvfp4[2])
         new.bias = None if self.bias is None else self.bias.clone()
         new.shared_gate_vec = None if self.shared_gate_vec is None else self.shared_gate_vec.clone()
         new.shared = [(pk.clone(), sc.clone(), s2) for pk, sc, s2 in self.shared]
@@ -96,7 +110,9 @@ class DeviceLayer:
         return new
 
     def nbytes(self) -> int:
-        n = self.router_w.numel() * 4 + (0 if self.shared_gate_vec is None else self.shared_gate_vec.numel() * 4)
+        n = (self.router_w.numel() * 4 if self.router_w is not None
+             else self.router_nvfp4[0].numel() + self.router_nvfp4[1].numel())
+        n += 0 if self.shared_gate_vec is None else self.shared_gate_vec.numel() * 4
         n += 0 if self.bias is None else self.bias.numel() * 4
         n += sum(pk.numel() + sc.numel() for pk, sc, _ in self.shared)
         n += sum(t.numel() for t in self.packed) + sum(t.numel() for t in self.scales)

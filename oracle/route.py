@@ -10,7 +10,8 @@ form (router GEMV then ``moe_topk_softmax``).
 
 Readings where the pages are silent (each is listed in the design notes):
 * the router input is the layer input itself (``router_input`` unexplained);
-* the router weight is dense fp32 [E, h];
+* the router weight is dense fp32 [E, h] (the configs' router), or NVFP4 like
+  the experts (the pages' other router form);
 * softmax selects on the logits (monotone in the probabilities);
 * sigmoid routing adds the bias to the sigmoid score for selection only, the
   weights use the unbiased score, the optional renormalisation comes first and
@@ -33,16 +34,25 @@ from typing import List, Tuple
 
 import numpy as np
 
-from .formats import bf16_to_f64, f64_to_f32
+from .formats import bf16_to_f64, dequant_nvfp4, f64_to_f32
 
 ROUTE_SOFTMAX = 0
 ROUTE_SIGMOID_BIAS = 1
 
 
-def router_logits(x_bits: np.ndarray, router_w: np.ndarray) -> np.ndarray:
-    """L[r, e] = fp32(sum_t x[r, t] * W[e, t]); bf16*fp32 products are exact in float64."""
+def router_logits(x_bits: np.ndarray, router_w) -> np.ndarray:
+    """L[r, e] = fp32(sum_t x[r, t] * W[e, t]); bf16*fp32 products are exact in float64.
+
+    ``router_w`` is a dense fp32 [E, h] array, or an NVFP4 matrix [E, h]
+    (an object with n, k, packed, scales, scale2): the gate projection is then
+    an NVFP4 GEMV/GEMM like the experts' (``forward_ep.rs`` calls
+    ``w4a16_decode_gemv``, ``forward_token_major.rs`` ``w4a16_gemm``, on the
+    router input).  Its weights are decoded exactly in float64 first."""
     x = bf16_to_f64(x_bits)
-    w = np.asarray(router_w, dtype=np.float32).astype(np.float64)
+    if hasattr(router_w, "packed"):
+        w = dequant_nvfp4(router_w.packed, router_w.scales, router_w.scale2, router_w.n, router_w.k)
+    else:
+        w = np.asarray(router_w, dtype=np.float32).astype(np.float64)
     return f64_to_f32(x @ w.T)
 
 

@@ -174,6 +174,20 @@ def router_weight(shape: MoeShape) -> np.ndarray:
     return w.astype(np.float32)
 
 
+# Mean of e2m1(c)^2 over the 16 codes: (0 + .25 + 1 + 2.25 + 4 + 9 + 16 + 36) / 8.
+_E2M1_MEAN_SQ = 8.5625
+
+
+def router_nvfp4(shape: MoeShape) -> Nvfp4Tensor:
+    """NVFP4 [E, h] router: codes and block scales drawn as for the experts, and
+    a per-tensor scale2 that brings the weights' variance to about 1/h, as the
+    fp32 router's N(0, 1/h): Var(w) = mean(e2m1^2) * E[scale^2] * scale2^2
+    with E[scale^2] = scale_sigma^2."""
+    t = nvfp4_random(shape, shape.num_experts, shape.hidden, KIND_ROUTER, 0, 1)
+    t.scale2 = float(np.float32(1.0 / math.sqrt(_E2M1_MEAN_SQ * shape.scale_sigma ** 2 * shape.hidden)))
+    return t
+
+
 def correction_bias(shape: MoeShape) -> Optional[np.ndarray]:
     """fp32 [E] ~ U(-0.1, 0.1) for sigmoid routing, else None."""
     if shape.route_kind != ROUTE_SIGMOID_BIAS:
@@ -215,7 +229,7 @@ def activations(shape: MoeShape, step: int = 0, rows: Optional[int] = None) -> n
 @dataclasses.dataclass
 class MoeLayerWeights:
     shape: MoeShape
-    router_w: np.ndarray
+    router_w: object  # fp32 [E, h] array, or an Nvfp4Tensor [E, h]
     bias: Optional[np.ndarray]
     shared_gate_vec: np.ndarray
     shared: Tuple[Nvfp4Tensor, Nvfp4Tensor, Nvfp4Tensor]
@@ -241,10 +255,14 @@ class MoeLayerWeights:
                 self._experts[key] = t
 
 
-def layer_weights(shape: MoeShape, materialise: bool = False, threads: int = 8) -> MoeLayerWeights:
+def layer_weights(shape: MoeShape, materialise: bool = False, threads: int = 8,
+                  router: str = "fp32") -> MoeLayerWeights:
+    """``router`` "fp32" (dense [E, h]) or "nvfp4" (an Nvfp4Tensor [E, h] in router_w)."""
+    if router not in ("fp32", "nvfp4"):
+        raise ValueError(router)
     w = MoeLayerWeights(
         shape=shape,
-        router_w=router_weight(shape),
+        router_w=router_weight(shape) if router == "fp32" else router_nvfp4(shape),
         bias=correction_bias(shape),
         shared_gate_vec=shared_gate_vector(shape),
         shared=tuple(shared_tensor(shape, p) for p in range(3)),

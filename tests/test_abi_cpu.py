@@ -226,3 +226,17 @@ def test_ep_refusals():
         assert u(lo, hi) == moe.MOE_ERR_INVALID_ARG, (lo, hi)
     assert lib.moe_union_local(X, 9, 8, 256, 0, 8, OUT, OUT + 512, OUT + 1024, OUT + 2048, None) == \
         moe.MOE_ERR_INVALID_ARG
+
+
+def test_router_refusals():
+    cfg = cfg_c4()
+    w = fake_weights()
+    w.router_nvfp4 = moe.MoeNvfp4(BASE + 0x500000, BASE + 0x540000, 1.0)   # both routers set
+    assert forward(cfg, w) == moe.MOE_ERR_INVALID_ARG
+    w = fake_weights()
+    w.router_w = 0                                                       # no router at all
+    assert forward(cfg, w) == moe.MOE_ERR_INVALID_ARG
+    w.router_nvfp4 = moe.MoeNvfp4(BASE + 0x500008, BASE + 0x540000, 1.0)  # misaligned codes
+    assert forward(cfg, w) == moe.MOE_ERR_INVALID_ARG
+    w.router_nvfp4 = moe.MoeNvfp4(BASE + 0x500000, BASE + 0x540000, float("nan"))
+    assert forward(cfg, w) == moe.MOE_ERR_INVALID_ARG

@@ -425,3 +425,15 @@ def test_ungated_shared_expert(name):
     assert np.all(read_intermediates(dl, ws, shape.rows)["gamma"] == 1.0)
     check_token_major(dl, x)
     check_ep_shares(weights, dl, x, [(0, shape.num_experts // 2), (shape.num_experts // 2, shape.num_experts)])
+
+
+
+# ---------------------------------------------------------------- NVFP4 router, whole layer
+@pytest.mark.parametrize("name", ["c1_e64_decode", "c2_e128_verify2"])
+def test_forward_nvfp4_router(name):
+    shape = synth.CONFIGS[name]
+    weights = synth.layer_weights(shape, router="nvfp4")
+    dl = upload(weights)
+    x = synth.activations(shape, 1)
+    check_against_oracle(weights, dl, x)
+    check_token_major(dl, x)

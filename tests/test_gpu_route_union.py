@@ -22,19 +22,26 @@ pytestmark = pytest.mark.gpu
 class RouteWeights:
     """Only the router-side tensors moe_route reads."""
 
-    def __init__(self, shape, router_w=None, bias=None, gate_vec=None):
+    def __init__(self, shape, router_w=None, bias=None, gate_vec=None, router="fp32"):
         torch = torch_cuda()
         moe = moe_mod()
         self.shape = shape
         self.cfg = moe.MoeConfig.from_shape(shape)
-        self.router_w_np = synth.router_weight(shape) if router_w is None else router_w
+        if router_w is None:
+            router_w = synth.router_weight(shape) if router == "fp32" else synth.router_nvfp4(shape)
+        self.router_w_np = router_w
         self.bias_np = synth.correction_bias(shape) if bias is None else bias
         self.gate_vec_np = synth.shared_gate_vector(shape) if gate_vec is None else gate_vec
-        self.router_w = torch.from_numpy(self.router_w_np).cuda()
         self.bias = None if self.bias_np is None else torch.from_numpy(self.bias_np).cuda()
         self.gate_vec = torch.from_numpy(self.gate_vec_np).cuda()
         w = moe.MoeWeights()
-        w.router_w = self.router_w.data_ptr()
+        if hasattr(router_w, "packed"):  # NVFP4 router
+            self.router_w = (torch.from_numpy(router_w.packed).cuda(), torch.from_numpy(router_w.scales).cuda())
+            w.router_nvfp4 = moe.MoeNvfp4(self.router_w[0].data_ptr(), self.router_w[1].data_ptr(),
+                                          float(router_w.scale2))
+        else:
+            self.router_w = torch.from_numpy(router_w).cuda()
+            w.router_w = self.router_w.data_ptr()
         w.correction_bias = 0 if self.bias is None else self.bias.data_ptr()
         w.shared_expert_gate = self.gate_vec.data_ptr()
         self.weights = w
@@ -184,3 +191,20 @@ def test_union_extremes():
     check_union(np.array([[255, 0, 128, 7]], np.int32), 256)              # one row
     check_union(np.array([[5], [5], [5]], np.int32), 16)                  # k = 1
     check_union(np.arange(64, dtype=np.int32)[::-1].reshape(1, 64), 64)   # k = 64, one row
+
+
+# ---------------------------------------------------------------- NVFP4 router
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_route_nvfp4_router(name):
+    shape = synth.CONFIGS[name]
+    rw = RouteWeights(shape, router="nvfp4")
+    for step in range(2):
+        check_route(rw, synth.activations(shape, step))
+
+
+def test_route_nvfp4_router_ragged():
+    # h with a partial 512-column router chunk; k = E; 64 ids
+    shape = synth.MoeShape("r", 2080, 12, 12, 96, 96, 5, synth.ROUTE_SIGMOID_BIAS, True, 2.5)
+    check_route(RouteWeights(shape, router="nvfp4"), synth.activations(shape, 3))
+    shape = synth.MoeShape("r2", 4160, 96, 8, 96, 96, 8, synth.ROUTE_SOFTMAX, False, 1.0)
+    check_route(RouteWeights(shape, router="nvfp4"), synth.activations(shape, 4))

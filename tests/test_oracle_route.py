@@ -120,3 +120,53 @@ def test_sigmoid_keys_fp32_add():
     k = RT.sigmoid_keys(L, bias)
     s32 = np.float32(1.0 / (1.0 + math.exp(-0.25)))
     assert k[0, 0] == np.float32(s32 + np.float32(0.01))
+
+
+# ---------------------------------------------------------------- NVFP4 router
+def _nvfp4_router(E, h, scale2, seed):
+    import synth
+    t = synth.nvfp4_random(synth.CONFIGS["c0_tiny"], E, h, 77, seed)
+    t.scale2 = scale2
+    return t
+
+
+def test_nvfp4_router_equals_dense_router_of_its_values():
+    # With a power-of-two scale2 every decoded weight (e2m1 * e4m3 * 2^-3, at
+    # most 6 significant bits) is an fp32 value, so the NVFP4 router must give
+    # the dense fp32 router's logits bit for bit.  The decode is checked by
+    # hand from the bit fields (low nibble = even column).
+    from oracle.formats import E2M1_TABLE, E4M3FN_TABLE
+    E, h = 12, 256
+    t = _nvfp4_router(E, h, 0.125, 1)
+    dense = np.zeros((E, h), np.float32)
+    for e in range(E):
+        for c in range(h):
+            byte = int(t.packed[e, c // 2])
+            code = (byte >> (4 * (c & 1))) & 0xF
+            dense[e, c] = np.float32(E2M1_TABLE[code] * E4M3FN_TABLE[int(t.scales[e, c // 16])] * 0.125)
+    x = _bf16_bits(np.random.default_rng(4).standard_normal((3, h)))
+    assert np.array_equal(RT.router_logits(x, t), RT.router_logits(x, dense))
+
+
+def test_nvfp4_router_logits_match_exact_sums():
+    from oracle.formats import dequant_nvfp4
+    E, h = 10, 512
+    t = _nvfp4_router(E, h, 0.0871, 2)   # scale2 not a power of two
+    x = _bf16_bits(np.random.default_rng(5).standard_normal((2, h)))
+    L = RT.router_logits(x, t)
+    W = dequant_nvfp4(t.packed, t.scales, t.scale2, E, h)
+    xf = bf16_to_f64(x)
+    for r in range(2):
+        for e in range(E):
+            ref = np.float32(math.fsum(float(a) * float(b) for a, b in zip(xf[r], W[e])))
+            assert abs(float(L[r, e]) - float(ref)) <= np.spacing(np.float32(abs(ref))), (r, e)
+
+
+def test_nvfp4_router_logit_scale():
+    # The generator's scale2 gives weights of variance about 1/h, so logits of
+    # N(0,1) rows have a standard deviation near 1, as with the fp32 router.
+    import synth
+    shape = synth.CONFIGS["c2_e128_verify2"]
+    t = synth.router_nvfp4(shape)
+    L = RT.router_logits(synth.activations(shape, 0), t)
+    assert 0.7 < float(np.std(L)) < 1.4
