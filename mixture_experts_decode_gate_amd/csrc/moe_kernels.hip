@@ -1082,19 +1082,36 @@ __global__ __launch_bounds__(256) void blend_kernel(const float* __restrict__ y,
                                                     const int32_t* __restrict__ slot_to_union,
                                                     const float* __restrict__ gamma, uint16_t* __restrict__ out,
                                                     float* __restrict__ partial, int h, int k) {
+  constexpr int kB = 8;  // slots whose loads are issued together
   const int r = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= h) return;
+  // The shared term's loads go out with the first batch; each batch issues
+  // all its slot-index and weight loads, then all its y loads, then adds in
+  // ascending j: a few memory round trips per thread instead of one per slot.
+  const float g = gamma[r];
+  const float ys = y[((size_t)kSharedSlot * kMaxRows + r) * h + n];
   float acc = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int s = slot_to_union[r * k + j];
-    if (s >= 0) acc = __builtin_fmaf(w[r * k + j], y[((size_t)s * kMaxRows + r) * h + n], acc);
+  for (int j0 = 0; j0 < k; j0 += kB) {
+    int sl[kB];
+    float wv[kB], yv[kB];
+#pragma unroll
+    for (int q = 0; q < kB; ++q) {
+      const int j = j0 + q < k ? j0 + q : k - 1;
+      sl[q] = j0 + q < k ? slot_to_union[r * k + j] : -1;
+      wv[q] = w[r * k + j];
+    }
+#pragma unroll
+    for (int q = 0; q < kB; ++q) yv[q] = y[((size_t)(sl[q] >= 0 ? sl[q] : 0) * kMaxRows + r) * h + n];
+#pragma unroll
+    for (int q = 0; q < kB; ++q)
+      if (sl[q] >= 0) acc = __builtin_fmaf(wv[q], yv[q], acc);
   }
   if (partial != nullptr) {
     partial[(size_t)r * h + n] = acc;
     return;
   }
-  acc = __builtin_fmaf(gamma[r], y[((size_t)kSharedSlot * kMaxRows + r) * h + n], acc);
+  acc = __builtin_fmaf(g, ys, acc);
   out[(size_t)r * h + n] = f32_to_bf16(acc);
 }
 
