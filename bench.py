@@ -36,7 +36,7 @@ METRIC = "routed-MoE layer µs/step + achieved HBM GB/s (% peak), rows=1..8, NVF
 # profiles/moe_forward_e256_rows8_pmc.md).  Valid only for the kernel sources it was taken on.
 TRAFFIC_SOURCES = ("mixture_experts_decode_gate_amd/csrc/moe_kernels.hip",
                    "mixture_experts_decode_gate_amd/csrc/moe_device.h")
-TRAFFIC_MEASURED = {"sources_sha256_16": "d65e03a967dc085a", "rows": 8, "gate_up_sweep_bytes": 794_685_542}
+TRAFFIC_MEASURED = {"sources_sha256_16": "88bbea8ecd5ddf95", "rows": 8, "gate_up_sweep_bytes": 794_616_525}
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "c4_e256_prefill8"
 N_INPUTS = 16
