@@ -1134,16 +1134,25 @@ __global__ __launch_bounds__(256) void ep_combine_kernel(const float* __restrict
 // ---------------------------------------------------------------- launchers
 namespace {
 
-int cu_count() {
-  static int cached[64] = {0};
+// Per-device launch caches hold this many devices; a device index past it is
+// served without caching.
+constexpr int kMaxDevices = 64;
+
+int current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  return dev;
+}
+
+int cu_count() {
+  static int cached[kMaxDevices] = {0};
+  const int dev = current_device();
+  if (dev >= 0 && dev < kMaxDevices && cached[dev]) return cached[dev];
+  int n = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev] = n;
+  return n;
 }
 
 int env_int(const char* name, int dflt) {
@@ -1161,8 +1170,12 @@ struct SweepShape {
   int per_cu = 0;
 };
 
+// ``caches`` is the calling kernel instance's per-device array of launch shapes.
 template <typename K>
-dim3 sweep_grid(K kernel, size_t lds, int max_blocks, SweepShape& cache, int default_threads) {
+dim3 sweep_grid(K kernel, size_t lds, int max_blocks, SweepShape (&caches)[kMaxDevices], int default_threads) {
+  const int dev = current_device();
+  SweepShape local;
+  SweepShape& cache = (dev >= 0 && dev < kMaxDevices) ? caches[dev] : local;
   if (cache.threads <= 0) {
     const int threads = default_threads;
     const int waves_per_cu = env_int("MOE_WAVES_PER_CU", 8);
@@ -1191,19 +1204,22 @@ hipError_t route_r(const RouteParams& p, bool do_topk, hipStream_t s) {
 template <int R, int NCH, int G>
 hipError_t gateup_rng(const SweepParams& p, int max_items, hipStream_t s) {
   const size_t lds = (size_t)R * NCH * kChunkUnits * 16;
-  static bool attr_set = false;
-  if (!attr_set) {
+  // The dynamic LDS limit is set once per device (the attribute is per device).
+  static bool attr_set[kMaxDevices] = {false};
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
     const hipError_t e = hipFuncSetAttribute((const void*)gateup_kernel<R, NCH, G>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
   }
-  static SweepShape shape;
-  const dim3 grid = sweep_grid(gateup_kernel<R, NCH, G>, lds, 1 << 30, shape, kMaxSweepThreads);
-  const int waves = (int)grid.x * (shape.threads / 64);
+  static SweepShape shapes[kMaxDevices];
+  const dim3 grid = sweep_grid(gateup_kernel<R, NCH, G>, lds, 1 << 30, shapes, kMaxSweepThreads);
+  const int threads = kMaxSweepThreads;
+  const int waves = (int)grid.x * (threads / 64);
   dim3 g = grid;
-  if (waves > max_items) g.x = (max_items * 64 + shape.threads - 1) / shape.threads;
-  hipLaunchKernelGGL((gateup_kernel<R, NCH, G>), g, dim3(shape.threads), lds, s, p);
+  if (waves > max_items) g.x = (max_items * 64 + threads - 1) / threads;
+  hipLaunchKernelGGL((gateup_kernel<R, NCH, G>), g, dim3(threads), lds, s, p);
   return hipGetLastError();
 }
 
@@ -1215,7 +1231,10 @@ hipError_t gateup_rn(const SweepParams& p, int max_items, hipStream_t s) {
 
 template <int R, int NCH>
 hipError_t down_rn(const SweepParams& p, int max_union, hipStream_t s) {
-  static int per_cu = 0;
+  static int per_cu_dev[kMaxDevices] = {0};
+  const int dev = current_device();
+  int local = 0;
+  int& per_cu = (dev >= 0 && dev < kMaxDevices) ? per_cu_dev[dev] : local;
   if (per_cu <= 0) {
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, down_kernel<R, NCH>, kDownThreads, 0) != hipSuccess ||
