@@ -160,6 +160,29 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, event_every=0
     return res
 
 
+def read_ceiling(nbytes=4 << 30, reps=5):
+    """Streaming-read rate of moe_read_probe over a buffer larger than the
+    Infinity Cache: the achievable ceiling for the weight sweeps' reads."""
+    import torch
+    import mixture_experts_decode_gate_amd as moe
+    from mixture_experts_decode_gate_amd.hip_events import HipEvent
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sink = torch.zeros(moe.moe_read_probe_sink_words(), dtype=torch.int32, device="cuda")
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    moe.moe_read_probe(src, sink)
+    e0, e1 = HipEvent(), HipEvent()
+    torch.cuda.synchronize()
+    e0.record(sh)
+    for _ in range(reps):
+        moe.moe_read_probe(src, sink)
+    e1.record(sh)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_ms(e1) / reps
+    del src, sink
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def ep_shares(cfg, layers, xs, shape, rows, n_ranks, steps, ws):
     """Time moe_forward_ep_partial for each of n_ranks equal expert ranges."""
     import torch
@@ -343,6 +366,8 @@ def main():
             f"us {[r['us_per_step'] for r in ep['ranges']]}")
 
     copy_gbps, _ = copy_reference()
+    read_gbps = read_ceiling()
+    log(f"[bench] streaming-read ceiling {read_gbps:.0f} GB/s; layer at {100 * res['gbps'] / read_gbps:.1f}% of it")
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(shape)
@@ -376,6 +401,8 @@ def main():
                      "timed_launches": st["launches"]},
         "stages_us": {k: round(v["avg_us"], 2) for k, v in res["stages"].items()},
         "copy_gbps": round(copy_gbps, 1),
+        "read_ceiling_gbps": round(read_gbps, 1),
+        "pct_of_read_ceiling": round(100 * res["gbps"] / read_gbps, 2),
         "sweep": sweep,
         "union_vs_token_major": ab,
         "ep_share": ep,

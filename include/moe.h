@@ -270,6 +270,15 @@ moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const 
                              uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes,
                              void* stream, void* const* stage_events);
 
+/* Measurement aid: the achievable streaming-read rate.  Reads every byte of
+ * src[0, bytes) once with the sweeps' 16-byte non-temporal loads and writes
+ * one fold word per block to sink[0, moe_read_probe_sink_words()).  Time it
+ * with events on ``stream``; bytes / time is the read ceiling the layer's
+ * weight sweeps are compared with.  src 16-byte aligned, bytes a positive
+ * multiple of 16; sink must not overlap src. */
+moe_status moe_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+int32_t moe_read_probe_sink_words(void);
+
 /* Number of kernel stages moe_forward enqueues, and the name of stage i
  * (NULL when out of range). */
 int32_t moe_num_stages(void);

@@ -10,6 +10,7 @@ libmoe.so.  The names match the C ABI in include/moe.h:
     moe_forward(cfg, w, x, out, ws)                  the whole layer
     moe_forward_token_major(cfg, w, x, out, ws)      the layer without the union (one slot per pair)
     moe_forward_timed(cfg, w, x, out, ws, events)    same, with per-stage events
+    moe_read_probe(src, sink)                        streaming-read ceiling (measurement aid)
     moe_union_local(topk_ids, lo, hi, union_ids, union_count, slot_to_union, row_mask, num_experts)
     moe_forward_ep_partial(cfg, w, x, partial, lo, hi, ws)   one GPU's expert-parallel share
     moe_ep_combine(cfg, reduced, out, ws)            shared expert added after the reduce
@@ -117,6 +118,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_ep_combine.argtypes = [P(MoeConfig), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t,
                                    C.c_void_p]
     lib.moe_ep_combine.restype = C.c_int
+    lib.moe_read_probe.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
+    lib.moe_read_probe.restype = C.c_int
+    lib.moe_read_probe_sink_words.argtypes = []
+    lib.moe_read_probe_sink_words.restype = C.c_int32
     lib.moe_forward_timed.argtypes = [P(MoeConfig), P(MoeWeights), C.c_void_p, C.c_void_p, C.c_int32,
                                       C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
     lib.moe_forward_timed.restype = C.c_int
@@ -211,6 +216,16 @@ def moe_forward_timed(cfg: MoeConfig, w: MoeWeights, x, out, ws, events: Sequenc
     arr = (ctypes.c_void_p * n)(*[(0 if e is None else int(getattr(e, "handle", e))) for e in ev[:n]])
     _check(load().moe_forward_timed(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(x.shape[0]),
                                     _ptr(ws), int(ws.numel() * ws.element_size()), _stream(stream), arr))
+
+
+def moe_read_probe(src, sink, stream=None) -> None:
+    """Read every byte of the device tensor ``src`` once (streaming-read ceiling);
+    ``sink`` holds at least moe_read_probe_sink_words() uint32 words."""
+    _check(load().moe_read_probe(_ptr(src), int(src.numel() * src.element_size()), _ptr(sink), _stream(stream)))
+
+
+def moe_read_probe_sink_words() -> int:
+    return int(load().moe_read_probe_sink_words())
 
 
 def moe_num_stages() -> int:

@@ -456,6 +456,20 @@ moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const 
   return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, stage_events, ForwardMode());
 }
 
+int32_t moe_read_probe_sink_words(void) { return moe::read_probe_blocks(); }
+
+moe_status moe_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !aligned(src, 16)) return fail(MOE_ERR_INVALID_ARG, "src must be a 16-byte aligned device pointer");
+  if (bytes == 0 || bytes % 16) return fail(MOE_ERR_INVALID_ARG, "bytes=%zu must be a positive multiple of 16", bytes);
+  if (!sink || !aligned(sink, 4)) return fail(MOE_ERR_INVALID_ARG, "sink must be a 4-byte aligned device pointer");
+  const int blocks = moe::read_probe_blocks();
+  if (overlaps(src, bytes, sink, (size_t)blocks * 4)) return fail(MOE_ERR_INVALID_ARG, "sink overlaps src");
+  hipError_t e = moe::launch_read_probe(static_cast<const uint8_t*>(src), bytes, sink, blocks,
+                                        reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_status(e, "probe launch");
+  return ok();
+}
+
 int32_t moe_num_stages(void) { return kNumStages; }
 
 const char* moe_stage_name(int32_t i) { return (i >= 0 && i < kNumStages) ? kStageNames[i] : nullptr; }

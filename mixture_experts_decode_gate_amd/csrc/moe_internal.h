@@ -81,6 +81,10 @@ hipError_t launch_blend(const float* y, const float* w, const int32_t* slot_to_u
                         uint16_t* out, float* partial, int rows, int h, int k, hipStream_t s);
 hipError_t launch_union_local(const int32_t* ids, int rows, int k, int lo, int hi, int32_t* union_ids,
                               int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);
+// Streaming-read probe over ``bytes`` (a multiple of 16) of ``src``; writes
+// one word per block to sink[0 .. blocks).
+hipError_t launch_read_probe(const uint8_t* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
+int read_probe_blocks();
 hipError_t launch_ep_combine(const float* reduced, const float* y, const float* gamma, uint16_t* out, int rows, int h,
                              hipStream_t s);
 

@@ -1131,6 +1131,41 @@ __global__ __launch_bounds__(256) void ep_combine_kernel(const float* __restrict
   out[(size_t)r * h + n] = f32_to_bf16(acc);
 }
 
+// Read-bandwidth probe: every 16-byte unit of ``src`` read once with the
+// sweeps' non-temporal 16-byte loads (each wave reads 1 KB contiguous per
+// load, waves grid-strided), folded by XOR into one word per block so the
+// loads cannot be dropped.  Measures the achievable streaming-read rate for
+// comparison with the sweeps' algorithmic GB/s.
+constexpr int kProbeThreads = 256;
+
+template <int kProbeUnroll>
+__global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const uint8_t* __restrict__ src, size_t units,
+                                                                   uint32_t* __restrict__ sink) {
+  __shared__ uint32_t s_x[kProbeThreads / 64];
+  const size_t stride = (size_t)gridDim.x * kProbeThreads;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  for (; i + (kProbeUnroll - 1) * stride < units; i += kProbeUnroll * stride) {
+    u32x4 v[kProbeUnroll];
+#pragma unroll
+    for (int q = 0; q < kProbeUnroll; ++q) v[q] = ld_stream(src + (i + q * stride) * 16);
+#pragma unroll
+    for (int q = 0; q < kProbeUnroll; ++q) acc ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;
+  }
+  for (; i < units; i += stride) {
+    const u32x4 v = ld_stream(src + i * 16);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+  if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < kProbeThreads / 64; ++w) t ^= s_x[w];
+    sink[blockIdx.x] = t;
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 namespace {
 
@@ -1349,6 +1384,21 @@ hipError_t launch_ep_combine(const float* reduced, const float* y, const float* 
   hipLaunchKernelGGL(ep_combine_kernel, grid, dim3(256), 0, s, reduced, y, gamma, out, h);
   return hipGetLastError();
 }
+
+hipError_t launch_read_probe(const uint8_t* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s) {
+  // Loads in flight per lane: 16 by default (the fastest of 4 / 8 / 16 measured
+  // on MI355X); MOE_PROBE_UNROLL overrides it for tuning runs.
+  switch (env_int("MOE_PROBE_UNROLL", 16)) {
+    case 4: hipLaunchKernelGGL(read_probe_kernel<4>, dim3(blocks), dim3(kProbeThreads), 0, s, src, bytes / 16, sink); break;
+    case 8: hipLaunchKernelGGL(read_probe_kernel<8>, dim3(blocks), dim3(kProbeThreads), 0, s, src, bytes / 16, sink); break;
+    default: hipLaunchKernelGGL(read_probe_kernel<16>, dim3(blocks), dim3(kProbeThreads), 0, s, src, bytes / 16, sink);
+  }
+  return hipGetLastError();
+}
+
+// 16 blocks per CU (half of them queued behind the resident ones) measured
+// fastest of 4 / 8 / 16; MOE_PROBE_BLOCKS_PER_CU overrides it for tuning runs.
+int read_probe_blocks() { return cu_count() * env_int("MOE_PROBE_BLOCKS_PER_CU", 16); }
 
 }  // namespace moe
 

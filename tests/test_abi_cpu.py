@@ -240,3 +240,12 @@ def test_router_refusals():
     assert forward(cfg, w) == moe.MOE_ERR_INVALID_ARG
     w.router_nvfp4 = moe.MoeNvfp4(BASE + 0x500000, BASE + 0x540000, float("nan"))
     assert forward(cfg, w) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_read_probe_refusals():
+    sink = OUT
+    assert lib.moe_read_probe(0, 4096, sink, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_read_probe(X + 8, 4096, sink, None) == moe.MOE_ERR_INVALID_ARG     # misaligned
+    assert lib.moe_read_probe(X, 0, sink, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_read_probe(X, 4100, sink, None) == moe.MOE_ERR_INVALID_ARG        # not a multiple of 16
+    assert lib.moe_read_probe(X, 4096, 0, None) == moe.MOE_ERR_INVALID_ARG

@@ -208,3 +208,21 @@ def test_route_nvfp4_router_ragged():
     check_route(RouteWeights(shape, router="nvfp4"), synth.activations(shape, 3))
     shape = synth.MoeShape("r2", 4160, 96, 8, 96, 96, 8, synth.ROUTE_SOFTMAX, False, 1.0)
     check_route(RouteWeights(shape, router="nvfp4"), synth.activations(shape, 4))
+
+
+# ---------------------------------------------------------------- streaming-read probe (measurement aid)
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 24) + 160])
+def test_read_probe_reads_every_word(nbytes):
+    # The blocks' fold words XOR to the XOR of every 32-bit word of the buffer:
+    # each word was read exactly once (a word read twice or skipped would
+    # change the fold for random contents).
+    torch = torch_cuda()
+    moe = moe_mod()
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = torch.zeros(moe.moe_read_probe_sink_words(), dtype=torch.int32, device="cuda")
+    moe.moe_read_probe(src, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)
