@@ -36,7 +36,7 @@ METRIC = "routed-MoE layer µs/step + achieved HBM GB/s (% peak), rows=1..8, NVF
 # profiles/moe_forward_e256_rows8_pmc.md).  Valid only for the kernel sources it was taken on.
 TRAFFIC_SOURCES = ("mixture_experts_decode_gate_amd/csrc/moe_kernels.hip",
                    "mixture_experts_decode_gate_amd/csrc/moe_device.h")
-TRAFFIC_MEASURED = {"sources_sha256_16": "88bbea8ecd5ddf95", "rows": 8, "gate_up_sweep_bytes": 794_616_525}
+TRAFFIC_MEASURED = {"sources_sha256_16": "0fa4d9085a164c4f", "rows": 8, "gate_up_sweep_bytes": 794_587_167}
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "c4_e256_prefill8"
 N_INPUTS = 16
@@ -158,6 +158,40 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, event_every=0
                                bytes_per_launch=b / len(traced), launches=len(traced))
         res["stages"] = stage
     return res
+
+
+def config_runs(steps, main_shape, main_layers, main_cfg, ws_main):
+    """µs/step and GB/s of moe_forward on each configuration at its own rows.
+    Every layer is copied on the device until a pass over the copies moves more
+    than 1 GB of the bytes a step touches, so steps read HBM rather than the
+    256 MB Infinity Cache.  The 256-expert configurations reuse the main
+    layer's copies."""
+    import torch
+    import mixture_experts_decode_gate_amd as moe
+    import synth
+    out = []
+    for name in synth.CONFIG_ORDER:
+        shape = synth.CONFIGS[name]
+        same = (shape.hidden, shape.num_experts, shape.moe_inter) == (main_shape.hidden, main_shape.num_experts,
+                                                                      main_shape.moe_inter)
+        if same:
+            cfg, layers, ws = main_cfg, main_layers, ws_main
+        else:
+            per_step = step_bytes(shape, shape.rows, min(shape.top_k * shape.rows, shape.num_experts))["layer"]
+            n_copies = int(min(64, max(2, -(-(1 << 30) // per_step))))
+            cfg, layers = build_layers(shape, n_copies)
+            ws = torch.zeros(moe.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+        xs = [torch.from_numpy(synth.activations(shape, s).view(np.int16)).cuda() for s in range(N_INPUTS)]
+        us = union_sizes(cfg, layers[0], xs, ws)
+        r = timed_run(cfg, layers, xs, us, shape, shape.rows, steps, 10, ws)
+        out.append(dict(config=name, rows=shape.rows, mean_union=round(r["mean_union"], 3), layer_copies=len(layers),
+                        us_per_step=round(r["us_per_step"], 2), gbps=round(r["gbps"], 1),
+                        pct_peak=round(100 * r["gbps"] / HBM_PEAK_GBPS, 2)))
+        log(f"[bench] config {name}: {r['us_per_step']:.1f} us/step, {r['gbps']:.0f} GB/s, U={r['mean_union']:.2f}")
+        if not same:
+            del layers, ws
+            torch.cuda.empty_cache()
+    return out
 
 
 def read_ceiling(nbytes=4 << 30, reps=5):
@@ -353,6 +387,8 @@ def main():
             log(f"[bench] A/B rows={R} ({kind}): union {a['us_per_step']:.1f} us (U={a['mean_union']:.2f}) vs "
                 f"token-major {b['us_per_step']:.1f} us ({R * shp.top_k} streams): x{ab[-1]['speedup']:.3f}")
 
+    configs = config_runs(args.sweep_steps, base_shape, layers, cfg, ws) if not args.no_sweep else []
+
     # One GPU's expert-parallel share at the real shape: the layer's 256
     # experts split over 8 GPUs, each sweeping its 32-expert range of the
     # union (plus the shared expert) and writing an fp32 partial.  Each range is
@@ -405,6 +441,7 @@ def main():
         "pct_of_read_ceiling": round(100 * res["gbps"] / read_gbps, 2),
         "sweep": sweep,
         "union_vs_token_major": ab,
+        "configs": configs,
         "ep_share": ep,
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
     }
