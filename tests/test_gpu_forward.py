@@ -437,3 +437,24 @@ def test_forward_nvfp4_router(name):
     x = synth.activations(shape, 1)
     check_against_oracle(weights, dl, x)
     check_token_major(dl, x)
+
+
+# ---------------------------------------------------------------- maximum sizes
+MAX_SHAPES = [
+    # hidden at its cap (four 2048-column chunks in the gate/up sweep) with 8 rows and 64 ids
+    synth.MoeShape("max_h_rows8", 8192, 16, 8, 64, 96, 8, synth.ROUTE_SIGMOID_BIAS, True, 2.5),
+    # hidden and both intermediates at their caps (two chunks in the down sweep)
+    synth.MoeShape("max_h_max_inter", 8192, 4, 2, 4096, 4096, 2, synth.ROUTE_SOFTMAX, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("shape", MAX_SHAPES, ids=[s.name for s in MAX_SHAPES])
+def test_maximum_sizes(shape):
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = synth.activations(shape, 0)
+    check_against_oracle(weights, dl, x)
+    singles = np.stack([run_forward(dl, x[r:r + 1])[0][0] for r in range(shape.rows)])
+    got, _ = run_forward(dl, x)
+    assert np.array_equal(got, singles)
+    check_token_major(dl, x)
