@@ -458,3 +458,33 @@ def test_maximum_sizes(shape):
     got, _ = run_forward(dl, x)
     assert np.array_equal(got, singles)
     check_token_major(dl, x)
+
+
+# ---------------------------------------------------------------- degenerate inputs
+def test_identical_rows_give_union_k_and_identical_outputs():
+    shape = dataclasses.replace(synth.CONFIGS["c2_e128_verify2"], rows=8, name="c2_rows8")
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = np.repeat(synth.activations(shape, 0)[:1], 8, axis=0)
+    got, ws = run_forward(dl, x)
+    mid = read_intermediates(dl, ws, 8)
+    assert mid["union_count"] == shape.top_k
+    assert np.all(mid["row_mask"] == 0xFF)
+    assert all(np.array_equal(got[r], got[0]) for r in range(8))
+    check_against_oracle(weights, dl, x, rows_checked=[0])
+
+
+def test_zero_row_routes_to_lowest_ids():
+    # x = 0: every logit is 0, softmax keys all tie and go to ids 0..k-1 with
+    # weights 1/k; the gate is sigmoid(0) = 0.5; every expert output is 0.
+    shape = synth.CONFIGS["c1_e64_decode"]
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = np.zeros((1, shape.hidden), np.uint16)
+    got, ws = run_forward(dl, x)
+    mid = read_intermediates(dl, ws, 1)
+    assert np.array_equal(mid["ids"][0], np.arange(shape.top_k))
+    assert np.all(mid["weights"][0] == np.float32(1.0 / shape.top_k))
+    assert mid["gamma"][0] == 0.5
+    assert np.all(got == 0)
+    check_against_oracle(weights, dl, x)
