@@ -488,3 +488,118 @@ def test_zero_row_routes_to_lowest_ids():
     assert mid["gamma"][0] == 0.5
     assert np.all(got == 0)
     check_against_oracle(weights, dl, x)
+
+
+# ---------------------------------------------------------------- guard bands and capture of every call
+GUARD = 4096  # bytes of 0xA5 before and after every output and the workspace
+
+
+def guarded(torch, nbytes):
+    """A device buffer with guard bands; returns (whole, inner view as uint8)."""
+    whole = torch.full((nbytes + 2 * GUARD,), 0xA5, dtype=torch.uint8, device="cuda")
+    return whole, whole[GUARD:GUARD + nbytes]
+
+
+def guards_intact(whole, nbytes):
+    host = whole.cpu().numpy()
+    return bool(np.all(host[:GUARD] == 0xA5) and np.all(host[GUARD + nbytes:] == 0xA5))
+
+
+@pytest.mark.parametrize("name", ["c0_tiny", "c2_e128_verify2"])
+def test_no_write_outside_buffers(name):
+    """Every entry point writes only inside its outputs and the workspace
+    (sized exactly to moe_workspace_bytes)."""
+    torch = torch_cuda()
+    moe = moe_mod()
+    shape = synth.CONFIGS[name]
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = x_dev(synth.activations(shape, 0))
+    R, h, k = shape.rows, shape.hidden, shape.top_k
+    wsn = moe.moe_workspace_bytes(dl.cfg)
+    ws_all, ws = guarded(torch, wsn)
+    ws.zero_()
+    out_all, out_u8 = guarded(torch, R * h * 2)
+    part_all, part_u8 = guarded(torch, R * h * 4)
+    ids_all, ids_u8 = guarded(torch, R * k * 4)
+    w_all, w_u8 = guarded(torch, R * k * 4)
+    uid_all, uid_u8 = guarded(torch, 64 * 4)
+    cnt_all, cnt_u8 = guarded(torch, 4)
+    s2u_all, s2u_u8 = guarded(torch, R * k * 4)
+    msk_all, msk_u8 = guarded(torch, 64 * 4)
+    out = out_u8.view(torch.int16).view(R, h)
+    part = part_u8.view(torch.float32).view(R, h)
+    ids = ids_u8.view(torch.int32).view(R, k)
+    moe.moe_forward(dl.cfg, dl.weights, x, out, ws)
+    moe.moe_forward_token_major(dl.cfg, dl.weights, x, out, ws)
+    moe.moe_forward_ep_partial(dl.cfg, dl.weights, x, part, 0, shape.num_experts // 2, ws)
+    moe.moe_ep_combine(dl.cfg, part, out, ws)
+    moe.moe_route(dl.cfg, dl.weights, x, ids, w_u8.view(torch.float32).view(R, k), ws)
+    moe.moe_union(ids, uid_u8.view(torch.int32), cnt_u8.view(torch.int32), s2u_u8.view(torch.int32),
+                  msk_u8.view(torch.int32), num_experts=shape.num_experts)
+    moe.moe_union_local(ids, 1, shape.num_experts - 1, uid_u8.view(torch.int32), cnt_u8.view(torch.int32),
+                        s2u_u8.view(torch.int32), msk_u8.view(torch.int32), num_experts=shape.num_experts)
+    torch.cuda.synchronize()
+    for whole, n in ((ws_all, wsn), (out_all, R * h * 2), (part_all, R * h * 4), (ids_all, R * k * 4),
+                     (w_all, R * k * 4), (uid_all, 256), (cnt_all, 4), (s2u_all, R * k * 4), (msk_all, 256)):
+        assert guards_intact(whole, n)
+
+
+def test_graph_capture_every_call():
+    """moe_route, moe_union, moe_forward_token_major, moe_forward_ep_partial and
+    moe_ep_combine captured into one graph replay like eager calls."""
+    torch = torch_cuda()
+    moe = moe_mod()
+    shape = synth.CONFIGS["c2_e128_verify2"]
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    R, h, k, E = shape.rows, shape.hidden, shape.top_k, shape.num_experts
+    xs = [synth.activations(shape, s) for s in range(3)]
+    x = x_dev(xs[0])
+    ws_a, ws_b = ws_for(dl.cfg), ws_for(dl.cfg)
+    ids = torch.zeros((R, k), dtype=torch.int32, device="cuda")
+    wts = torch.zeros((R, k), dtype=torch.float32, device="cuda")
+    uid = torch.zeros(64, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s2u = torch.zeros(R * k, dtype=torch.int32, device="cuda")
+    tm = torch.zeros((R, h), dtype=torch.int16, device="cuda")
+    part = torch.zeros((R, h), dtype=torch.float32, device="cuda")
+    comb = torch.zeros((R, h), dtype=torch.int16, device="cuda")
+
+    def calls():
+        moe.moe_route(dl.cfg, dl.weights, x, ids, wts, ws_a)
+        moe.moe_union(ids, uid, cnt, s2u, num_experts=E)
+        moe.moe_forward_token_major(dl.cfg, dl.weights, x, tm, ws_a)
+        moe.moe_forward_ep_partial(dl.cfg, dl.weights, x, part, 0, E, ws_b)
+        moe.moe_ep_combine(dl.cfg, part, comb, ws_b)
+
+    def snapshot():
+        # union_ids past U are left untouched by moe_union: compare the first U
+        snap = [t.cpu().numpy().copy() for t in (ids, wts, uid, cnt, s2u, tm, part, comb)]
+        snap[2] = snap[2][:int(snap[3][0])]
+        return snap
+
+    eager = []
+    for xb in xs:
+        x.copy_(x_dev(xb))
+        calls()
+        torch.cuda.synchronize()
+        eager.append(snapshot())
+    calls()  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(6):
+        x.copy_(x_dev(xs[rep % 3]))
+        for t in (ids, wts, uid, cnt, s2u, tm, part, comb):
+            t.zero_()
+        _ = torch.ones(1 << 20, device="cuda").sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(snapshot(), eager[rep % 3]):
+            assert np.array_equal(a, b), rep
+    # the full-range share plus the combine reproduces moe_forward
+    out, _ = run_forward(dl, xs[0])
+    assert np.array_equal(eager[0][7].view(np.uint16), out)
