@@ -34,8 +34,11 @@ def dequant(t) -> np.ndarray:
 
 
 def silu(z: np.ndarray) -> np.ndarray:
+    """z / (1 + exp(-z)); for z far below zero exp(-z) overflows to inf and the
+    quotient is the limit -0.0 (the overflow warning is silenced, not the value)."""
     z = np.asarray(z, dtype=np.float64)
-    return z / (1.0 + np.exp(-z))
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
 
 
 def ffn_dense(w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, x64: np.ndarray) -> np.ndarray:
