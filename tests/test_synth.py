@@ -66,13 +66,18 @@ def test_distributions():
 
 
 @pytest.mark.slow
-def test_c3_mean_union_near_pages_k4_curve():
-    # Statistical property of the workload (not a parity pin): the mean union
-    # over 200 steps stays near the 23.35 the pages report at K = 4.
+@pytest.mark.parametrize("K,pages", [(2, 13.74), (3, 18.76), (4, 23.35)])
+def test_c3_mean_union_near_pages_curve(K, pages):
+    # Statistical property of the workload (not a parity pin): the row
+    # correlation was tuned to the K = 4 union of the "Function forward_moe"
+    # rustdoc's "amortize PARTIALLY" note (8.00 / 13.74 / 18.76 / 23.35 at
+    # K = 1..4); the same workload's first K rows follow the rest of that curve
+    # (400 steps: 13.59 / 18.67 / 23.38).  Means over 200 steps.
+    import dataclasses
     import importlib.util, os
     spec = importlib.util.spec_from_file_location(
         "tune", os.path.join(os.path.dirname(__file__), "golden", "tune_c3_row_corr.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
-    m, _ = mod.mean_union(synth.CONFIGS["c3_e256_verify4"], steps=200)
-    assert abs(m - 23.35) < 0.6
+    m, _ = mod.mean_union(dataclasses.replace(synth.CONFIGS["c3_e256_verify4"], rows=K), steps=200)
+    assert abs(m - pages) < 0.6
