@@ -374,7 +374,8 @@ def main():
     ab = []
     if not args.no_sweep:
         c3 = synth.CONFIGS["c3_e256_verify4"]
-        cases = [(base_shape.with_rows(R), R, "independent") for R in range(1, 9)] + [(c3, 4, "correlated a=0.58")]
+        cases = [(base_shape.with_rows(R), R, "independent") for R in range(1, 9)] + [
+            (c3.with_rows(K) if K != c3.rows else c3, K, "correlated a=0.58") for K in (2, 3, 4)]
         for shp, R, kind in cases:
             xr = [torch.from_numpy(synth.activations(shp, s, rows=R).view(np.int16)).cuda() for s in range(N_INPUTS)]
             ur = union_sizes(cfg, layers[0], xr, ws)
