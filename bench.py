@@ -12,8 +12,15 @@ finds another step's weights in the 256 MB Infinity Cache).
 Prints one JSON line: value = achieved HBM GB/s from algorithmic bytes (each
 step's own union size) over the timed wall time of K steps; per-stage HIP
 events recorded on the launch stream inside the same timed region give the
-dominant kernel's roofline figure.  Also reports the rows=1..8 sweep and the
-CPU oracle timed on a bounded sample (a reference point, not the target).
+dominant kernel's roofline figure.  Also reports, in the same line:
+  sweep                 rows=1..8 at the same shape
+  configs               every layer configuration at its own rows
+  union_vs_token_major  the union sweep against moe_forward_token_major on the
+                        same inputs (independent rows 1..8, correlated K=2..4)
+  ep_share              one GPU's expert-parallel share (8 ranges of 32 experts)
+  read_ceiling_gbps     moe_read_probe's streaming-read rate over 4 GiB
+  cpu_baseline          the CPU oracle timed on a bounded sample (a reference
+                        point, not the target)
 """
 
 from __future__ import annotations
