@@ -220,6 +220,18 @@ moe_status moe_union_local(const int32_t* topk_ids, int32_t rows, int32_t top_k,
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                        uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream);
 
+/* The layer over any number of rows, in sub-chunks of min(MOE_MAX_ROWS,
+ * MOE_MAX_IDS / top_k) consecutive rows, each one moe_forward on ``stream``
+ * with ``ws``, in row order ("Function forward_moe" rustdoc, "WIDENED
+ * (2026-08-31)" note: the 8-row batched prefill sub-chunk amortises its
+ * routed experts over its own union).  x[rows, h] in, out[rows, h] out; rows
+ * >= 1.  Arguments, refusals and ownership as moe_forward (x and out must not
+ * overlap each other or the workspace).  Since every row's output depends on
+ * that row alone, out is byte-identical to one-row calls.  The workspace holds
+ * the last sub-chunk's intermediates. */
+moe_status moe_forward_prefill(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                               uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream);
+
 /* The layer without the union: every (row, selected expert) pair is its own
  * slot, so an expert chosen by several rows is streamed once per row
  * (metrale_model_layers/layers/moe/forward_token_major.rs,

@@ -9,6 +9,7 @@ libmoe.so.  The names match the C ABI in include/moe.h:
     moe_union(topk_ids, union_ids, union_count, slot_to_union, row_mask, num_experts)
     moe_forward(cfg, w, x, out, ws)                  the whole layer
     moe_forward_token_major(cfg, w, x, out, ws)      the layer without the union (one slot per pair)
+    moe_forward_prefill(cfg, w, x, out, ws)          any number of rows, in 8-row sub-chunks
     moe_forward_timed(cfg, w, x, out, ws, events)    same, with per-stage events
     moe_read_probe(src, sink)                        streaming-read ceiling (measurement aid)
     moe_union_local(topk_ids, lo, hi, union_ids, union_count, slot_to_union, row_mask, num_experts)
@@ -107,6 +108,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward.argtypes = [P(MoeConfig), P(MoeWeights), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
                                 C.c_size_t, C.c_void_p]
     lib.moe_forward.restype = C.c_int
+    lib.moe_forward_prefill.argtypes = lib.moe_forward.argtypes
+    lib.moe_forward_prefill.restype = C.c_int
     lib.moe_forward_token_major.argtypes = lib.moe_forward.argtypes
     lib.moe_forward_token_major.restype = C.c_int
     lib.moe_union_local.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
@@ -179,6 +182,12 @@ def moe_forward(cfg: MoeConfig, w: MoeWeights, x, out, ws, stream=None) -> None:
     """x [rows, h] bf16 -> out [rows, h] bf16 (device tensors); ws a uint8 device tensor."""
     _check(load().moe_forward(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(x.shape[0]), _ptr(ws),
                               int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def moe_forward_prefill(cfg: MoeConfig, w: MoeWeights, x, out, ws, stream=None) -> None:
+    """x [rows, h] bf16 (any rows >= 1) -> out [rows, h] bf16, in 8-row sub-chunks."""
+    _check(load().moe_forward_prefill(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(x.shape[0]),
+                                      _ptr(ws), int(ws.numel() * ws.element_size()), _stream(stream)))
 
 
 def moe_forward_token_major(cfg: MoeConfig, w: MoeWeights, x, out, ws, stream=None) -> None:

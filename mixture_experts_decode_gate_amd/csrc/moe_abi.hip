@@ -410,6 +410,28 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16
   return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, nullptr, ForwardMode());
 }
 
+moe_status moe_forward_prefill(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                               uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream) {
+  if (rows < 1) return fail(MOE_ERR_INVALID_ARG, "rows=%d must be positive", rows);
+  moe_status st = check_config(cfg);
+  if (st) return st;
+  const int chunk = MOE_MAX_IDS / cfg->top_k < MOE_MAX_ROWS ? MOE_MAX_IDS / cfg->top_k : MOE_MAX_ROWS;
+  if (!x_bf16 || !out_bf16) return fail(MOE_ERR_INVALID_ARG, "x and out must be device pointers");
+  const size_t xb = (size_t)rows * cfg->hidden * sizeof(uint16_t);
+  if (overlaps(x_bf16, xb, out_bf16, xb)) return fail(MOE_ERR_INVALID_ARG, "x and out overlap");
+  if (ws && overlaps(x_bf16, xb, ws, ws_bytes)) return fail(MOE_ERR_INVALID_ARG, "x overlaps the workspace");
+  if (ws && overlaps(out_bf16, xb, ws, ws_bytes)) return fail(MOE_ERR_INVALID_ARG, "out overlaps the workspace");
+  // Each sub-chunk is one moe_forward on the same stream and workspace, in row
+  // order; every argument check runs on the first sub-chunk before any launch.
+  for (int32_t r0 = 0; r0 < rows; r0 += chunk) {
+    const int32_t n = rows - r0 < chunk ? rows - r0 : chunk;
+    const size_t off = (size_t)r0 * cfg->hidden;
+    st = forward_impl(cfg, w, x_bf16 + off, out_bf16 + off, n, ws, ws_bytes, stream, nullptr, ForwardMode());
+    if (st) return st;
+  }
+  return ok();
+}
+
 moe_status moe_forward_token_major(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                                    uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream) {
   ForwardMode m;

@@ -249,3 +249,18 @@ def test_read_probe_refusals():
     assert lib.moe_read_probe(X, 0, sink, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_read_probe(X, 4100, sink, None) == moe.MOE_ERR_INVALID_ARG        # not a multiple of 16
     assert lib.moe_read_probe(X, 4096, 0, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_prefill_refusals():
+    cfg = cfg_c4()
+    need = lib.moe_workspace_bytes(ctypes.byref(cfg))
+    pf = lambda rows, x=X, out=OUT, w=None, ws_bytes=need: lib.moe_forward_prefill(
+        ctypes.byref(cfg), ctypes.byref(w or fake_weights()), x, out, rows, WS, ws_bytes, None)
+    assert pf(0) == moe.MOE_ERR_INVALID_ARG
+    assert pf(-3) == moe.MOE_ERR_INVALID_ARG
+    assert pf(40, out=X + 6144 * 2 * 20) == moe.MOE_ERR_INVALID_ARG   # out overlaps x
+    assert pf(40, x=WS + 4096) == moe.MOE_ERR_INVALID_ARG             # x inside the workspace
+    assert pf(40, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    w = fake_weights()
+    w.router_w = BASE + 0x1004
+    assert pf(40, w=w) == moe.MOE_ERR_INVALID_ARG

@@ -603,3 +603,30 @@ def test_graph_capture_every_call():
     # the full-range share plus the combine reproduces moe_forward
     out, _ = run_forward(dl, xs[0])
     assert np.array_equal(eager[0][7].view(np.uint16), out)
+
+
+# ---------------------------------------------------------------- more rows than one block: prefill sub-chunks
+PREFILL = [
+    (dataclasses.replace(synth.CONFIGS["c2_e128_verify2"], rows=20, name="c2_rows20"), [0, 9, 19]),
+    (synth.MoeShape("k16_rows11", 512, 32, 16, 64, 96, 11, synth.ROUTE_SIGMOID_BIAS, True, 2.5), None),
+]
+
+
+@pytest.mark.parametrize("shape,rows_checked", PREFILL, ids=[s.name for s, _ in PREFILL])
+def test_prefill_sub_chunks(shape, rows_checked):
+    torch = torch_cuda()
+    moe = moe_mod()
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x_bits = synth.activations(shape, 0, rows=shape.rows)
+    x = x_dev(x_bits)
+    out = torch.zeros_like(x)
+    moe.moe_forward_prefill(dl.cfg, dl.weights, x, out, ws_for(dl.cfg))
+    torch.cuda.synchronize()
+    got = out_bits(out)
+    singles = np.stack([run_forward(dl, x_bits[r:r + 1])[0][0] for r in range(shape.rows)])
+    assert np.array_equal(got, singles)
+    ref = moe_layer_from(weights, x_bits, rows=rows_checked)
+    rows = ref["rows"]
+    rel_l2, rel_max = output_errors(got[rows], ref["out"][rows])
+    assert np.all(rel_l2 <= REL_L2_TOL) and np.all(rel_max <= REL_MAX_TOL), (rel_l2, rel_max)
