@@ -14,7 +14,8 @@ step's own union size) over the timed wall time of K steps; per-stage HIP
 events recorded on the launch stream inside the same timed region give the
 dominant kernel's roofline figure.  Also reports, in the same line:
   sweep                 rows=1..8 at the same shape
-  configs               every layer configuration at its own rows
+  configs               every layer configuration at its own rows (also replayed
+                        from a captured HIP graph: device time without launch cost)
   union_vs_token_major  the union sweep against moe_forward_token_major on the
                         same inputs (independent rows 1..8, correlated K=2..4)
   ep_share              one GPU's expert-parallel share (8 ranges of 32 experts)
@@ -191,14 +192,43 @@ def config_runs(steps, main_shape, main_layers, main_cfg, ws_main):
         xs = [torch.from_numpy(synth.activations(shape, s).view(np.int16)).cuda() for s in range(N_INPUTS)]
         us = union_sizes(cfg, layers[0], xs, ws)
         r = timed_run(cfg, layers, xs, us, shape, shape.rows, steps, 10, ws)
+        g_us = graph_step_us(cfg, layers, xs, ws)
         out.append(dict(config=name, rows=shape.rows, mean_union=round(r["mean_union"], 3), layer_copies=len(layers),
                         us_per_step=round(r["us_per_step"], 2), gbps=round(r["gbps"], 1),
-                        pct_peak=round(100 * r["gbps"] / HBM_PEAK_GBPS, 2)))
-        log(f"[bench] config {name}: {r['us_per_step']:.1f} us/step, {r['gbps']:.0f} GB/s, U={r['mean_union']:.2f}")
+                        pct_peak=round(100 * r["gbps"] / HBM_PEAK_GBPS, 2), graph_us_per_step=round(g_us, 2)))
+        log(f"[bench] config {name}: {r['us_per_step']:.1f} us/step, {r['gbps']:.0f} GB/s, U={r['mean_union']:.2f}; "
+            f"graph replay {g_us:.1f} us/step")
         if not same:
             del layers, ws
             torch.cuda.empty_cache()
     return out
+
+
+def graph_step_us(cfg, layers, xs, ws, n_steps=32, reps=10):
+    """µs per step with n_steps moe_forward calls (cycling inputs and layer
+    copies) captured once in a HIP graph and replayed: the device-side step time
+    without per-call host launch cost."""
+    import torch
+    import mixture_experts_decode_gate_amd as moe
+    from mixture_experts_decode_gate_amd.hip_events import HipEvent
+    outs = [torch.empty_like(xs[0]) for _ in range(2)]
+    for i in range(4):  # warm-up outside capture
+        moe.moe_forward(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], outs[i % 2], ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_steps):
+            moe.moe_forward(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], outs[i % 2], ws)
+    g.replay()
+    torch.cuda.synchronize()
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    e0, e1 = HipEvent(), HipEvent()
+    e0.record(sh)
+    for _ in range(reps):
+        g.replay()
+    e1.record(sh)
+    torch.cuda.synchronize()
+    return e0.elapsed_ms(e1) * 1e3 / (reps * n_steps)
 
 
 def read_ceiling(nbytes=4 << 30, reps=5):
