@@ -630,3 +630,30 @@ def test_prefill_sub_chunks(shape, rows_checked):
     rows = ref["rows"]
     rel_l2, rel_max = output_errors(got[rows], ref["out"][rows])
     assert np.all(rel_l2 <= REL_L2_TOL) and np.all(rel_max <= REL_MAX_TOL), (rel_l2, rel_max)
+
+
+# ---------------------------------------------------------------- per-stage events
+def test_forward_timed_matches_forward_and_times_every_stage():
+    torch = torch_cuda()
+    moe = moe_mod()
+    from mixture_experts_decode_gate_amd.hip_events import HipEvent
+    shape = synth.CONFIGS["c2_e128_verify2"]
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x_bits = synth.activations(shape, 4)
+    want, _ = run_forward(dl, x_bits)
+    x = x_dev(x_bits)
+    n = moe.moe_num_stages()
+    assert moe.moe_stage_names() == ["route", "gate_up_sweep", "down_sweep", "blend"]
+    for events in ([HipEvent() for _ in range(n + 1)], [None] * (n + 1), [HipEvent(), None, HipEvent(), None, None]):
+        out = torch.zeros_like(x)
+        moe.moe_forward_timed(dl.cfg, dl.weights, x, out, ws_for(dl.cfg), events)
+        torch.cuda.synchronize()
+        assert np.array_equal(out_bits(out), want)
+    ev = [HipEvent() for _ in range(n + 1)]
+    out = torch.zeros_like(x)
+    moe.moe_forward_timed(dl.cfg, dl.weights, x, out, ws_for(dl.cfg), ev)
+    torch.cuda.synchronize()
+    stages = [ev[i].elapsed_ms(ev[i + 1]) for i in range(n)]
+    assert all(t >= 0.0 for t in stages) and stages[1] > 0.0
+    assert abs(sum(stages) - ev[0].elapsed_ms(ev[n])) <= 1e-3 + 1e-3 * ev[0].elapsed_ms(ev[n])
