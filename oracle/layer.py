@@ -36,7 +36,10 @@ from .union import expert_union, expert_union_local
 
 
 def blend_row(w_row: np.ndarray, y_row: np.ndarray, gamma: float, shared_row: np.ndarray) -> np.ndarray:
-    """bf16(fp32(sum_j w[j] * y[j] + gamma * shared)), the j-sum in float64 in ascending j."""
+    """bf16(fp32(sum_j w[j] * y[j] + gamma * shared)), the j-sum in float64 in ascending j.
+
+    Pinned with routing weights other than 1 (and distinct within a row) by a
+    closed-form layer in tests/test_oracle_layer.py."""
     acc = np.zeros(y_row.shape[-1], dtype=np.float64)
     for j in range(len(w_row)):
         acc = acc + float(w_row[j]) * y_row[j].astype(np.float64)

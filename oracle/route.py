@@ -24,7 +24,9 @@ Readings where the pages are silent (each is listed in the design notes):
 
 Pinned by tests/test_oracle_route.py: brute-force exact dot products
 (math.fsum) for the logits; numpy's stable argsort for the selection order
-including ties; closed forms for a zero router; sums of renormalised weights.
+including ties; closed forms for a zero router; sums of renormalised weights;
+the k-th/(k+1)-th key margin against constructed keys and a brute force over
+every k-subset.
 """
 
 from __future__ import annotations
@@ -137,8 +139,22 @@ def route(x_bits, router_w, bias, route_kind: int, k: int, norm_topk_prob: bool,
     return L, ids, w
 
 
+def selection_keys(logits32: np.ndarray, bias, route_kind: int) -> np.ndarray:
+    """The fp32 keys top-k compares: the logits for softmax routing, fp32(fp32(s) + bias)
+    for sigmoid routing."""
+    if route_kind == ROUTE_SOFTMAX:
+        return np.asarray(logits32, dtype=np.float32)
+    if route_kind == ROUTE_SIGMOID_BIAS:
+        return sigmoid_keys(logits32, bias)
+    raise ValueError(f"unknown route kind {route_kind}")
+
+
 def topk_margin(keys32: np.ndarray, k: int) -> float:
-    """Gap between the k-th and (k+1)-th largest key of a row (inf if k == E)."""
+    """Gap between the k-th and (k+1)-th largest key of a row (inf if k == E).
+
+    The selection is unique when the gap is positive; a gap below the rounding
+    noise of an independent evaluation of the logits marks a near-tie, where two
+    correct implementations may pick different experts."""
     v = np.sort(np.asarray(keys32, dtype=np.float64))[::-1]
     if k >= len(v):
         return math.inf

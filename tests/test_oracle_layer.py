@@ -124,3 +124,70 @@ def test_ep_partials_reduce_to_the_layer():
     out = ep_combine(red.astype(np.float32), full["gamma"], full["shared_y"])
     g, ref = bf16_to_f64(out), bf16_to_f64(full["out"])
     assert np.all(np.abs(g - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30)
+
+
+# ---------------------------------------------------------------- weighted sum, top_k >= 2
+# A layer whose routing weights and expert outputs are known in closed form, so
+# the weighted sum of moe_weighted_sum_blend_prefill (forward_token_major.rs:
+# out = sum_j w[r, j] * y[r, j] + gate * shared) is checked with weights other
+# than 1 and with distinct weights inside a row.
+#
+# Row r's input is bf16 1.0 at column r and zero elsewhere, and router row e is
+# zero except at columns 0 and 1, so the logits are exactly L[r, e] = W[e, r].
+# Logits of +100, 0 and -100 give sigmoid scores of exactly 1 and 0.5 in
+# float64 (exp(-100) is below half an ulp of 1) and a score below 1e-43; the
+# small distinct biases order equal scores.  With renormalisation the weights
+# are s_j / sum(s) * routed_scaling_factor:
+#   row 0 selects experts 6, 5 (score 1) and 2 (score 0.5): w = 1, 1, 0.5
+#   row 1 selects expert 0 (score 1), then 4 and 3 (score 0.5): w = 1.25, 0.625, 0.625
+# Every expert has all-ones codes and block scales 1.0 with its own power-of-two
+# scale2 c_e, so for a one-hot input g = v = c_e and y_e = I * c_e * fp32(silu(c_e) * c_e)
+# in every column (the all-ones closed form of the FFN).  A zero gate vector gives
+# gamma = 0.5; the shared expert is all ones with scale2 1.
+_WS_C = [1.0, 2.0, 4.0, 0.5, 0.25, 8.0, 0.125, 16.0]
+_WS_L = [[-100.0, -100.0, 0.0, -100.0, -100.0, 100.0, 100.0, -100.0],
+         [100.0, -100.0, -100.0, 0.0, 0.0, -100.0, -100.0, -100.0]]
+_WS_IDS = [[6, 5, 2], [0, 4, 3]]
+_WS_W = [[1.0, 1.0, 0.5], [1.25, 0.625, 0.625]]
+
+
+def _weighted_sum_layer():
+    h, E, k, I = 64, 8, 3, 32
+    s = synth.MoeShape("wsum", h, E, k, I, I, 2, synth.ROUTE_SIGMOID_BIAS, True, 2.5)
+
+    def ones(n, kk, scale2):
+        return synth.Nvfp4Tensor(n, kk, np.full((n, kk // 2), 0x22, np.uint8),
+                                 np.full((n, kk // 16), 0x38, np.uint8), scale2)
+
+    router = np.zeros((E, h), np.float32)
+    router[:, 0], router[:, 1] = _WS_L[0], _WS_L[1]
+    bias = (0.01 * np.arange(E) - 0.04).astype(np.float32)
+    w = synth.MoeLayerWeights(shape=s, router_w=router, bias=bias, shared_gate_vec=np.zeros(h, np.float32),
+                              shared=(ones(I, h, 1.0), ones(I, h, 1.0), ones(h, I, 1.0)))
+    w._experts = {(e, p): ones(I, h, _WS_C[e]) if p < 2 else ones(h, I, _WS_C[e])
+                  for e in range(E) for p in range(3)}
+    w.lazy = False
+    x = np.zeros((2, h), np.uint16)
+    x[0, 0] = x[1, 1] = 0x3F80  # bf16 1.0
+    return s, w, x
+
+
+def _all_ones_y(c, inter):
+    a = float(np.float32(c / (1.0 + math.exp(-c)) * c))
+    return inter * c * a  # exact: I and c are powers of two
+
+
+def test_weighted_sum_closed_form_top_k_3():
+    s, w, x = _weighted_sum_layer()
+    o = moe_layer_from(w, x)
+    assert o["ids"].tolist() == _WS_IDS
+    assert o["weights"].tolist() == _WS_W
+    assert np.all(o["gamma"] == 0.5)
+    shared = _all_ones_y(1.0, s.shared_inter)
+    for r in range(2):
+        # every term is an fp32 value times a short dyadic weight, and their
+        # exponents span far less than float64's 53 bits: the sum is exact
+        total = sum(_WS_W[r][j] * _all_ones_y(_WS_C[_WS_IDS[r][j]], s.moe_inter) for j in range(s.top_k))
+        total += 0.5 * shared
+        want = f32_to_bf16_bits(np.full(s.hidden, total, np.float64).astype(np.float32))
+        assert np.array_equal(o["out"][r], want), (r, bf16_to_f64(o["out"][r][:1]), total)

@@ -4,8 +4,10 @@ Each case patches one plausible error into the oracle (swapped nibbles, an
 exponent bias off by one, silu on the wrong projection, a dropped shared
 term, ties broken the wrong way, a sorted union, renormalising over all
 experts, biased sigmoid weights, a local union without its range filter, a
-rank's partial that keeps remote slots, an ungated shared expert dropped) and
-runs the pin that should catch it.
+rank's partial that keeps remote slots, an ungated shared expert dropped, a
+weighted sum that ignores the routing weights or pairs them with the wrong
+slots, a near-tie margin taken between the wrong ranks) and runs the pin that
+should catch it.
 """
 
 import numpy as np
@@ -169,3 +171,31 @@ def test_ungated_shared_as_zero_caught(monkeypatch):
     monkeypatch.setattr(LY, "shared_gate", zero_when_ungated)
     with pytest.raises(AssertionError):
         T_layer.test_ungated_shared_expert_is_gate_one()
+
+
+def test_weights_ignored_caught(monkeypatch):
+    real = LY.blend_row
+    # the mistake: every routed expert enters the sum with weight 1
+    monkeypatch.setattr(LY, "blend_row", lambda w_row, y_row, gamma, shared_row: real(
+        np.ones_like(w_row), y_row, gamma, shared_row))
+    with pytest.raises(AssertionError):
+        T_layer.test_weighted_sum_closed_form_top_k_3()
+
+
+def test_weights_paired_with_reversed_slots_caught(monkeypatch):
+    real = LY.blend_row
+    # the mistake: weight j multiplies the output of slot k - 1 - j
+    monkeypatch.setattr(LY, "blend_row", lambda w_row, y_row, gamma, shared_row: real(
+        w_row[::-1], y_row, gamma, shared_row))
+    with pytest.raises(AssertionError):
+        T_layer.test_weighted_sum_closed_form_top_k_3()
+
+
+def test_margin_between_wrong_ranks_caught(monkeypatch):
+    def off_by_one(keys32, k):
+        v = np.sort(np.asarray(keys32, dtype=np.float64))[::-1]
+        # the mistake: ranks k+1 and k+2 instead of k and k+1
+        return float(v[k] - v[k + 1]) if k + 1 < len(v) else float("inf")
+    monkeypatch.setattr(RT, "topk_margin", off_by_one)
+    with pytest.raises(AssertionError):
+        T_route.test_topk_margin_constructed_keys()

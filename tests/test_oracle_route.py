@@ -170,3 +170,37 @@ def test_nvfp4_router_logit_scale():
     t = synth.router_nvfp4(shape)
     L = RT.router_logits(synth.activations(shape, 0), t)
     assert 0.7 < float(np.std(L)) < 1.4
+
+
+def test_topk_margin_constructed_keys():
+    keys = np.array([3.0, 1.0, 2.0, 2.0], np.float32)
+    assert RT.topk_margin(keys, 1) == 1.0  # 3 vs 2
+    assert RT.topk_margin(keys, 2) == 0.0  # an exact tie between ranks 2 and 3
+    assert RT.topk_margin(keys, 3) == 1.0  # 2 vs 1
+    assert RT.topk_margin(keys, 4) == math.inf
+
+
+def test_topk_margin_is_best_subset_gap():
+    # Brute force over every k-subset S: the margin is the largest value of
+    # min(keys in S) - max(keys outside S), reached by the selected set.
+    import itertools
+    rng = np.random.default_rng(21)
+    for trial in range(60):
+        E = int(rng.integers(2, 8))
+        k = int(rng.integers(1, E))
+        keys = rng.standard_normal(E).astype(np.float32)
+        best = max(min(float(keys[e]) for e in S) - max(float(keys[e]) for e in range(E) if e not in S)
+                   for S in itertools.combinations(range(E), k))
+        assert RT.topk_margin(keys, k) == best
+        sel = RT.select_topk(keys, k)
+        assert min(float(keys[e]) for e in sel) - max(float(keys[e]) for e in range(E) if e not in sel) == best
+
+
+def test_selection_keys_by_route_kind():
+    L = np.array([[0.0, 1.0, -2.0]], np.float32)
+    bias = np.array([0.25, -0.125, 0.0], np.float32)
+    assert np.array_equal(RT.selection_keys(L, None, RT.ROUTE_SOFTMAX), L)
+    # sigmoid(0) = 0.5 exactly: key 0.75; the others through sigmoid_keys
+    k = RT.selection_keys(L, bias, RT.ROUTE_SIGMOID_BIAS)
+    assert k[0, 0] == np.float32(0.75)
+    assert np.array_equal(k, RT.sigmoid_keys(L, bias))
