@@ -10,8 +10,11 @@ experts), rows=8 independent N(0,1) rows.  Steps cycle over 16 seeded inputs
 finds another step's weights in the 256 MB Infinity Cache).
 
 Prints one JSON line: value = achieved HBM GB/s from algorithmic bytes (each
-step's own union size) over the timed wall time of K steps; per-stage HIP
-events recorded on the launch stream inside the same timed region give the
+step's own union size) over the device time of K back-to-back steps, measured
+by two HIP events on the launch stream with nothing else enqueued between the
+steps.  A second pass of K steps launches every kernel with its own start and
+stop events (hipExtLaunchKernel: the kernel's own execution, nothing
+enqueued between kernels) and gives each stage's average kernel duration: the
 dominant kernel's roofline figure.  Also reports, in the same line:
   sweep                 rows=1..8 at the same shape
   configs               every layer configuration at its own rows (also replayed
@@ -84,7 +87,11 @@ def step_bytes(shape, rows: int, U: int) -> dict:
     # whole layer: weights + router + bias + gate vector + x in + out
     layer = (U * 3 * expert_bytes(I, h) + 3 * expert_bytes(Is, h) + 4 * E * h
              + (4 * E if shape.route_kind == 1 else 0) + 4 * h + 4 * rows * h)
-    return dict(layer=layer, route=route, gate_up_sweep=gateup, down_sweep=down, blend=blend)
+    # down sweep and blend in one stage: weights, activations, out (plus the weights
+    # and gates of the blend); the expert outputs are an intermediate of the two-kernel form
+    down_blend = U * expert_bytes(h, I) + expert_bytes(Is, h) + 2 * (pairs * I + rows * Is) + 2 * rows * h + 8 * pairs
+    return dict(layer=layer, route=route, gate_up_sweep=gateup, down_sweep=down, blend=blend,
+                down_sweep_blend=down_blend)
 
 
 def build_layers(shape, n_layers: int):
@@ -104,27 +111,29 @@ def build_layers(shape, n_layers: int):
     return cfg, layers
 
 
-def union_sizes(cfg, layer, xs, ws):
+def union_sizes(cfg, layers, xs, ws):
+    """Union size of each input (one moe_forward per input; the inputs cycle
+    over the layer copies so every copy has been run once before timing)."""
     import torch
     import mixture_experts_decode_gate_amd as moe
     L = moe.moe_workspace_layout(cfg)
     out = torch.empty_like(xs[0])
     us = []
-    for x in xs:
-        moe.moe_forward(cfg, layer.weights, x, out, ws)
+    for i in range(max(len(xs), len(layers))):
+        moe.moe_forward(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], out, ws)
         torch.cuda.synchronize()
-        us.append(int(ws[L.union_count:L.union_count + 4].cpu().numpy().view(np.int32)[0]))
+        if i < len(xs):
+            us.append(int(ws[L.union_count:L.union_count + 4].cpu().numpy().view(np.int32)[0]))
     return us
 
 
-def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, event_every=0, token_major=False):
+def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, stage_events=False, token_major=False):
     """K back-to-back steps between two events on the launch stream.  With
-    event_every > 0, every event_every-th step is launched through
-    moe_forward_timed, which records an event before and after each stage of
-    that step on the same stream (stage durations for the roofline); the other
-    steps run moe_forward unchanged.  With token_major, every step runs
-    moe_forward_token_major (no union); its bytes are still counted with the
-    union's U, so GB/s compares the two paths on the same useful work."""
+    stage_events, every step is launched through moe_forward_timed, whose
+    kernels each record a start and a stop event (their own execution): the
+    per-stage kernel durations for the roofline.  With token_major, every step
+    runs moe_forward_token_major (no union); its bytes are still counted with
+    the union's U, so GB/s compares the two paths on the same useful work."""
     import torch
     import mixture_experts_decode_gate_amd as moe
     from mixture_experts_decode_gate_amd.hip_events import HipEvent
@@ -133,13 +142,17 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, event_every=0
     sh = int(stream.cuda_stream)
     out = torch.empty_like(xs[0])
     nst = moe.moe_num_stages()
-    for i in range(warmup):
-        fwd(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], out, ws)
-    traced = [i for i in range(steps) if event_every and i % event_every == 0]
-    events = {i: [HipEvent() for _ in range(nst + 1)] for i in traced}
+    traced = list(range(steps)) if stage_events else []
+    events = {i: [HipEvent() for _ in range(2 * nst)] for i in traced}
     start, end = HipEvent(), HipEvent()
+    # Barrier before the warm-up, then the warm-up steps and the timed steps
+    # back to back: the start event is taken when the device finishes the last
+    # warm-up step, so the device never idles before the timed steps (an idle
+    # gap measurably slows the next steps while the clocks recover).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(warmup):
+        fwd(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], out, ws)
     start.record(sh)
     for i in range(steps):
         lay, xi = layers[i % len(layers)], i % len(xs)
@@ -160,7 +173,7 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, event_every=0
         names = moe.moe_stage_names()
         stage = {}
         for s, name in enumerate(names):
-            d = [events[i][s].elapsed_ms(events[i][s + 1]) for i in traced]
+            d = [events[i][2 * s].elapsed_ms(events[i][2 * s + 1]) for i in traced]
             b = sum(sbytes[i][name] for i in traced)
             stage[name] = dict(avg_us=float(np.mean(d)) * 1e3, gbps=b / (sum(d) * 1e-3) / 1e9,
                                bytes_per_launch=b / len(traced), launches=len(traced))
@@ -190,7 +203,7 @@ def config_runs(steps, main_shape, main_layers, main_cfg, ws_main):
             cfg, layers = build_layers(shape, n_copies)
             ws = torch.zeros(moe.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
         xs = [torch.from_numpy(synth.activations(shape, s).view(np.int16)).cuda() for s in range(N_INPUTS)]
-        us = union_sizes(cfg, layers[0], xs, ws)
+        us = union_sizes(cfg, layers, xs, ws)
         r = timed_run(cfg, layers, xs, us, shape, shape.rows, steps, 10, ws)
         g_us = graph_step_us(cfg, layers, xs, ws)
         out.append(dict(config=name, rows=shape.rows, mean_union=round(r["mean_union"], 3), layer_copies=len(layers),
@@ -351,8 +364,6 @@ def main():
     ap.add_argument("--rows", type=int, default=8)
     ap.add_argument("--layers", type=int, default=8, help="device copies of the layer cycled by the steps")
     ap.add_argument("--sweep-steps", type=int, default=100)
-    ap.add_argument("--event-every", type=int, default=4,
-                    help="record per-stage events on every n-th timed step (0: none)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for rocprofv3: no sweep, no CPU leg")
@@ -389,17 +400,19 @@ def main():
                 for s in range(N_INPUTS)]
 
     xs = inputs(args.rows)
-    us = union_sizes(cfg, layers[0], xs, ws)
+    us = union_sizes(cfg, layers, xs, ws)
     log(f"[bench] unions over {N_INPUTS} inputs: {us}")
-    res = timed_run(cfg, layers, xs, us, shape, args.rows, args.steps, args.warmup, ws,
-                    event_every=args.event_every)
+    res = timed_run(cfg, layers, xs, us, shape, args.rows, args.steps, args.warmup, ws)
     log(f"[bench] rows={args.rows}: {res['us_per_step']:.1f} us/step, {res['gbps']:.0f} GB/s")
+    # the same K steps again, every kernel with its own start and stop events
+    staged = timed_run(cfg, layers, xs, us, shape, args.rows, args.steps, args.warmup, ws, stage_events=True)
+    log("[bench] kernel durations: " + ", ".join(f"{k} {v['avg_us']:.2f} us" for k, v in staged["stages"].items()))
 
     sweep = []
     if not args.no_sweep:
         for R in range(1, 9):
             xr = inputs(R)
-            ur = union_sizes(cfg, layers[0], xr, ws)
+            ur = union_sizes(cfg, layers, xr, ws)
             r = timed_run(cfg, layers, xr, ur, base_shape.with_rows(R), R, args.sweep_steps, 10, ws)
             sweep.append(dict(rows=R, us_per_step=round(r["us_per_step"], 2), gbps=round(r["gbps"], 1),
                               frac=round(r["gbps"] / HBM_PEAK_GBPS, 4), mean_union=r["mean_union"]))
@@ -415,7 +428,7 @@ def main():
             (c3.with_rows(K) if K != c3.rows else c3, K, "correlated a=0.58") for K in (2, 3, 4)]
         for shp, R, kind in cases:
             xr = [torch.from_numpy(synth.activations(shp, s, rows=R).view(np.int16)).cuda() for s in range(N_INPUTS)]
-            ur = union_sizes(cfg, layers[0], xr, ws)
+            ur = union_sizes(cfg, layers, xr, ws)
             a = timed_run(cfg, layers, xr, ur, shp, R, args.sweep_steps, 10, ws)
             b = timed_run(cfg, layers, xr, ur, shp, R, args.sweep_steps, 10, ws, token_major=True)
             ab.append(dict(rows=R, rows_kind=kind, mean_union=a["mean_union"], pairs=R * shp.top_k,
@@ -448,7 +461,7 @@ def main():
         log(f"[bench] cpu oracle: {cpu['sample']}: {cpu['value']:.3f} GB/s")
 
     dom = "gate_up_sweep"
-    st = res["stages"][dom]
+    st = staged["stages"][dom]
     line = {
         "metric": METRIC,
         "value": round(res["gbps"], 2),
@@ -472,8 +485,11 @@ def main():
                      "unit": "GB/s", "frac": round(st["gbps"] / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(args.rows),
                      "avg_launch_us": round(st["avg_us"], 2), "bytes_per_launch": int(st["bytes_per_launch"]),
-                     "timed_launches": st["launches"]},
-        "stages_us": {k: round(v["avg_us"], 2) for k, v in res["stages"].items()},
+                     "timed_launches": st["launches"],
+                     "timing": "kernel start/stop events (hipExtLaunchKernel) in a second pass of the same steps"},
+        "stages_us": {k: round(v["avg_us"], 2) for k, v in staged["stages"].items()},
+        "stages_gbps": {k: round(v["gbps"], 1) for k, v in staged["stages"].items()},
+        "staged_pass_us_per_step": round(staged["us_per_step"], 2),
         "copy_gbps": round(copy_gbps, 1),
         "read_ceiling_gbps": round(read_gbps, 1),
         "pct_of_read_ceiling": round(100 * res["gbps"] / read_gbps, 2),

@@ -30,7 +30,8 @@
  *              router_w dense fp32, or the NVFP4 router_nvfp4 decoded exactly)
  *   softmax: ids = top_k of L[r,:]; w = softmax weights of those ids,
  *            renormalised over the k ids when norm_topk_prob.
- *   sigmoid: s = sigmoid(L); ids = top_k of fp32(s + bias);
+ *   sigmoid: s = sigmoid(L); ids = top_k of fp32(fp32(s) + bias) (s rounded
+ *            to fp32, then an fp32 add);
  *            w = s[ids] (renormalised when norm_topk_prob) * routed_scaling_factor.
  *   ids within a row are ordered by descending key, equal keys by lower id.
  *   FFN_e(x) = W_down[e] @ (silu(W_gate[e] @ x) * (W_up[e] @ x))
@@ -144,16 +145,14 @@ typedef struct moe_weights {
 
 /* Byte offsets of the intermediates moe_forward leaves in the workspace.
  * The layout depends on the config only (sized for MOE_MAX_ROWS rows).
- * Offsets are multiples of 256.
+ * Offsets are multiples of 256.  The workspace needs no initialisation: every
+ * call writes what it reads.  Calls sharing one workspace must not overlap in
+ * time (same stream, or ordered by events).
  *
- * The workspace must be zero-filled (its first 256 bytes suffice) before
- * its first use: the routing kernel counts its finished blocks in the first
- * word (the last block to finish runs top-k and the union) and resets that
- * word before it ends, so a workspace is zeroed once, not per call.  Calls
- * sharing one workspace must not overlap in time (same stream, or ordered
- * by events). */
+ * Expert activations and outputs are stored by (row, selected expert) pair:
+ * pair t = r*k + j holds row r's j-th routed expert, pair rows*k + r row r's
+ * shared expert. */
 typedef struct moe_ws_layout {
-  size_t sync;          /* uint32 [1]                 arrival counter, zero between calls */
   size_t logits;        /* float  [MOE_MAX_ROWS][E]   router logits (row stride E)    */
   size_t score;         /* double [MOE_MAX_ROWS][E]   sigmoid(logit) for sigmoid routing */
   size_t gamma;         /* float  [MOE_MAX_ROWS]      sigmoid(x_r . shared gate)      */
@@ -165,14 +164,14 @@ typedef struct moe_ws_layout {
   size_t row_mask;      /* uint32 [MOE_MAX_IDS]       bit r: row r chose union expert */
   size_t slot_info;     /* internal per-union-slot weight pointers                    */
   size_t segments;      /* internal down-sweep work table                             */
-  size_t act;           /* bf16   [MOE_MAX_IDS+1][MOE_MAX_ROWS][Imax] silu(g)*u,
-                           slot MOE_MAX_IDS = shared expert, Imax = max(I, Is)       */
-  size_t y;             /* float  [MOE_MAX_IDS+1][MOE_MAX_ROWS][h] expert outputs     */
+  size_t act;           /* bf16   [MOE_MAX_IDS+MOE_MAX_ROWS][Imax] silu(g)*u by pair,
+                           Imax = max(I, Is); pairs rows*(k+1) and up unused          */
+  size_t y;             /* float  [MOE_MAX_IDS+MOE_MAX_ROWS][h] expert outputs by pair */
   size_t total;         /* bytes needed                                               */
 } moe_ws_layout;
 
 /* Workspace bytes for ``cfg`` (any rows up to MOE_MAX_ROWS); 0 if cfg is
- * invalid.  Zero-fill the workspace once before its first use. */
+ * invalid.  The workspace may hold anything before a call. */
 size_t moe_workspace_bytes(const moe_config* cfg);
 
 /* Fill ``out`` with the workspace layout of ``cfg``. */
@@ -274,10 +273,12 @@ moe_status moe_forward_ep_partial(const moe_config* cfg, const moe_weights* w, c
 moe_status moe_ep_combine(const moe_config* cfg, const float* reduced, uint16_t* out_bf16, int32_t rows, void* ws,
                           size_t ws_bytes, void* stream);
 
-/* moe_forward that also records ``stage_events[i]`` (a hipEvent_t, may be
- * NULL) on ``stream`` before stage i, and ``stage_events[moe_num_stages()]``
- * after the last stage: per-stage timing without changing the work.
- * ``stage_events`` itself may be NULL (then identical to moe_forward). */
+/* moe_forward whose stage i kernel records ``stage_events[2i]`` (a
+ * hipEvent_t, may be NULL) when it starts and ``stage_events[2i+1]`` when it
+ * ends (hipExtLaunchKernel's start and stop events: the kernel's own
+ * execution, with nothing enqueued between kernels).  2 * moe_num_stages()
+ * entries.  ``stage_events`` itself may be NULL (then identical to
+ * moe_forward). */
 moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                              uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes,
                              void* stream, void* const* stage_events);

@@ -33,7 +33,9 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID_BIAS = 0, 1
 MOE_MAX_ROWS, MOE_MAX_IDS, MOE_MAX_EXPERTS, MOE_MAX_DIM, MOE_MAX_INTER = 8, 64, 1024, 8192, 4096
-SHARED_SLOT = MOE_MAX_IDS
+# Expert activations and outputs in the workspace are stored by (row, expert)
+# pair: pair r*k + j is row r's j-th routed expert, rows*k + r row r's shared expert.
+MAX_PAIRS = MOE_MAX_IDS + MOE_MAX_ROWS
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
                 4: "MOE_ERR_DEVICE"}
@@ -76,7 +78,7 @@ class MoeWeights(ctypes.Structure):
 
 class MoeWsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "sync", "logits", "score", "gamma", "topk_ids", "topk_w", "union_ids", "union_count", "slot_to_union",
+        "logits", "score", "gamma", "topk_ids", "topk_w", "union_ids", "union_count", "slot_to_union",
         "row_mask", "slot_info", "segments", "act", "y", "total")]
 
 
@@ -218,9 +220,9 @@ def moe_ep_combine(cfg: MoeConfig, reduced, out, ws, stream=None) -> None:
 
 
 def moe_forward_timed(cfg: MoeConfig, w: MoeWeights, x, out, ws, events: Sequence, stream=None) -> None:
-    """moe_forward recording events[i] before stage i and events[moe_num_stages()] after the last.
+    """moe_forward whose stage i kernel records events[2i] at its start and events[2i+1] at its end.
     ``events`` holds hipEvent_t handles (ints, objects with a ``handle`` attribute, or None)."""
-    n = moe_num_stages() + 1
+    n = 2 * moe_num_stages()
     ev = list(events) + [None] * n
     arr = (ctypes.c_void_p * n)(*[(0 if e is None else int(getattr(e, "handle", e))) for e in ev[:n]])
     _check(load().moe_forward_timed(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(x.shape[0]),

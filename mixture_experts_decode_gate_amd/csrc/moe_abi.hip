@@ -42,8 +42,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-const char* const kStageNames[] = {"route", "gate_up_sweep", "down_sweep", "blend"};
-constexpr int kNumStages = 4;
+// Stage 2 is one kernel (down sweep and blend together) when every pair's
+// activations fit in LDS, else the down sweep and then the blend kernel.
+const char* const kStageNames[] = {"route", "gate_up_sweep", "down_sweep_blend"};
+constexpr int kNumStages = 3;
 
 moe_status check_config(const moe_config* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
@@ -142,7 +144,6 @@ void compute_layout(const moe_config* c, moe_ws_layout* L) {
     off = round_up(off + bytes, 256);
     return o;
   };
-  L->sync = take(moe::kSyncBytes);
   L->logits = take(R * E * sizeof(float));
   L->score = take(R * E * sizeof(double));
   L->gamma = take(R * sizeof(float));
@@ -155,8 +156,8 @@ void compute_layout(const moe_config* c, moe_ws_layout* L) {
   L->slot_info = take((MOE_MAX_IDS + 1) * moe::kSlotInfoBytes);
   L->segments = take(sizeof(int32_t) + (size_t)moe::kMaxDownSegs * (sizeof(int32_t) + sizeof(uint32_t)) +
                      (size_t)(moe::kMaxDownSegs + 1) * sizeof(int32_t));
-  L->act = take((MOE_MAX_IDS + 1) * R * imax * sizeof(uint16_t));
-  L->y = take((MOE_MAX_IDS + 1) * R * h * sizeof(float));
+  L->act = take((size_t)moe::kMaxPairs * imax * sizeof(uint16_t));
+  L->y = take((size_t)moe::kMaxPairs * h * sizeof(float));
   L->total = off;
 }
 
@@ -241,7 +242,6 @@ void fill_route(moe::RouteParams& p, const moe_config* c, const moe_weights* w, 
   p.gamma = reinterpret_cast<float*>(ws + L.gamma);
   p.ids_out = ids_out;
   p.w_out = w_out;
-  p.counter = reinterpret_cast<uint32_t*>(ws + L.sync);
   p.union_ids = reinterpret_cast<int32_t*>(ws + L.union_ids);
   p.union_count = reinterpret_cast<int32_t*>(ws + L.union_count);
   p.slot_to_union = reinterpret_cast<int32_t*>(ws + L.slot_to_union);
@@ -290,9 +290,14 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(ws);
-  auto mark = [&](int i) -> hipError_t {
-    if (events && events[i]) return hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s);
-    return hipSuccess;
+  // Stage i's kernel records events[2i] at its start and events[2i+1] at its end.
+  auto stage_ev = [&](int i) {
+    moe::StageEvents ev;
+    if (events) {
+      ev.start = reinterpret_cast<hipEvent_t>(events[2 * i]);
+      ev.stop = reinterpret_cast<hipEvent_t>(events[2 * i + 1]);
+    }
+    return ev;
   };
   // Slots the sweeps may see: the union holds at most min(k*rows, E) experts;
   // the token-major list holds every one of the k*rows pairs.
@@ -321,19 +326,23 @@ moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const uint1
   sp.seg_rows = reinterpret_cast<uint32_t*>(sp.seg_slot + moe::kMaxDownSegs);
   sp.seg_cum = reinterpret_cast<int32_t*>(sp.seg_rows + moe::kMaxDownSegs);
   sp.token_major = token_major ? 1 : 0;
+  sp.out = out;
+  sp.partial = mode.partial;
 
   hipError_t e;
-  if ((e = mark(0)) != hipSuccess) return device_status(e, "event record");
-  if ((e = moe::launch_route(rp, false, s)) != hipSuccess) return device_status(e, "route launch");
-  if ((e = mark(1)) != hipSuccess) return device_status(e, "event record");
-  if ((e = moe::launch_gateup(sp, rows, max_slots, s)) != hipSuccess) return device_status(e, "gate/up launch");
-  if ((e = mark(2)) != hipSuccess) return device_status(e, "event record");
-  if ((e = moe::launch_down(sp, rows, max_slots, s)) != hipSuccess) return device_status(e, "down launch");
-  if ((e = mark(3)) != hipSuccess) return device_status(e, "event record");
+  if ((e = moe::launch_route(rp, s, stage_ev(0))) != hipSuccess) return device_status(e, "route launch");
+  if ((e = moe::launch_gateup(sp, rows, max_slots, s, stage_ev(1))) != hipSuccess)
+    return device_status(e, "gate/up launch");
+  const moe::StageEvents ev2 = stage_ev(2);
+  const int nr = moe::down_blend_rows_per_block(rows, cfg->top_k, cfg->hidden, sp.act_stride);
+  if (nr > 0) {
+    if ((e = moe::launch_down_blend(sp, rows, nr, s, ev2)) != hipSuccess) return device_status(e, "down+blend launch");
+    return ok();
+  }
+  if ((e = moe::launch_down(sp, s, {ev2.start, nullptr})) != hipSuccess) return device_status(e, "down launch");
   e = moe::launch_blend(sp.y, wts, rp.slot_to_union, reinterpret_cast<const float*>(wsb + L.gamma), out,
-                        mode.partial, rows, cfg->hidden, cfg->top_k, s);
+                        mode.partial, rows, cfg->hidden, cfg->top_k, s, {nullptr, ev2.stop});
   if (e != hipSuccess) return device_status(e, "blend launch");
-  if ((e = mark(4)) != hipSuccess) return device_status(e, "event record");
   return ok();
 }
 
@@ -375,8 +384,9 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   moe::RouteParams rp;
   fill_route(rp, cfg, w, x_bf16, rows, wsb, L, topk_ids, topk_w);
-  hipError_t e = moe::launch_route(rp, true, s);
+  hipError_t e = moe::launch_route(rp, s);
   if (e != hipSuccess) return device_status(e, "route launch");
+  if ((e = moe::launch_topk(rp, s)) != hipSuccess) return device_status(e, "top-k launch");
   return ok();
 }
 
@@ -467,7 +477,7 @@ moe_status moe_ep_combine(const moe_config* cfg, const float* reduced, uint16_t*
   char* wsb = static_cast<char*>(ws);
   hipError_t e = moe::launch_ep_combine(reduced, reinterpret_cast<const float*>(wsb + L.y),
                                         reinterpret_cast<const float*>(wsb + L.gamma), out_bf16, rows, cfg->hidden,
-                                        reinterpret_cast<hipStream_t>(stream));
+                                        cfg->top_k, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_status(e, "combine launch");
   return ok();
 }

@@ -14,7 +14,7 @@ constexpr int kChunk = 2048;        // K columns one wave covers per pass: 64 la
 constexpr int kChunkUnits = 256;    // 16-byte bf16 units per chunk (2048 * 2 B / 16 B)
 constexpr int kMaxRows = 8;
 constexpr int kMaxIds = 64;
-constexpr int kSharedSlot = 64;     // act / y / slot_info index of the shared expert
+constexpr int kSharedSlot = 64;     // slot table index of the shared expert
 constexpr int kNumSlots = 65;
 
 // Weight pointers of one union slot (a routed expert, or the shared expert at
@@ -32,6 +32,7 @@ struct SlotInfo {
   int32_t inter;      // rows of gate/up, columns of down
   uint32_t row_mask;  // bit r: row r uses this slot
   int32_t expert;     // expert id, -1 for the shared expert
+  uint8_t pair[kMaxRows];  // pair index of (this slot, row r) where row r uses the slot
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }

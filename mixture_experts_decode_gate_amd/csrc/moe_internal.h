@@ -10,9 +10,10 @@ namespace moe {
 
 struct SlotInfo;
 
-// Sync words at the start of the workspace: word 0 is the routing kernel's
-// arrival counter, zero between calls.
-constexpr size_t kSyncBytes = 256;
+// Expert activations and outputs are stored by (row, selected expert) pair:
+// pair t = r * k + j for row r's j-th routed expert, rows * k + r for row r's
+// shared expert.
+constexpr int kMaxPairs = MOE_MAX_IDS + MOE_MAX_ROWS;
 constexpr int kDownGroup = 2;  // act rows a down segment carries
 constexpr int kMaxDownSegs = (MOE_MAX_IDS + 1) * ((MOE_MAX_ROWS + kDownGroup - 1) / kDownGroup);
 // Down-sweep work weight of a segment with n rows: kSegCostBase + n per
@@ -36,7 +37,6 @@ struct RouteParams {
   float* gamma;            // [8]
   int32_t* ids_out;        // [rows][k]
   float* w_out;            // [rows][k]
-  uint32_t* counter;       // arrival counter: zero between calls
   // union outputs (moe_forward only)
   int32_t* union_ids;
   int32_t* union_count;
@@ -54,8 +54,8 @@ struct SweepParams {
   const uint16_t* x;          // [rows][h] bf16
   const SlotInfo* slots;      // [65] (down sweep; written by the gate/up sweep)
   const int32_t* union_count; // device U (down sweep)
-  uint16_t* act;              // [65][8][act_stride] bf16
-  float* y;                   // [65][8][h] fp32
+  uint16_t* act;              // [pairs][act_stride] bf16, by (row, expert) pair
+  float* y;                   // [pairs][h] fp32, by (row, expert) pair
   int h;
   int act_stride;             // max(inter, shared_inter)
   int inter;                  // routed expert intermediate size
@@ -66,26 +66,42 @@ struct SweepParams {
   int32_t* seg_cum;           // [kMaxDownSegs + 1] down segments: weight before segment s
   int32_t* seg_count;         // [1]
   int token_major;            // 1: one slot per (row, selected expert), no dedup
+  uint16_t* out;              // [rows][h] bf16 (down+blend kernel), or null with partial
+  float* partial;             // [rows][h] fp32 routed partial (expert-parallel share), or null
 };
 
-constexpr size_t kSlotInfoBytes = 72;  // sizeof(SlotInfo), checked in the kernels file
+constexpr size_t kSlotInfoBytes = 80;  // sizeof(SlotInfo), checked in the kernels file
 
-hipError_t launch_route(const RouteParams& p, bool do_topk, hipStream_t s);
+// Optional kernel start/stop events (hipExtLaunchKernel): the events record
+// the kernel's own start and end, with nothing enqueued between kernels.
+struct StageEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Router GEMV: logits, sigmoid scores and the shared-expert gate.
+hipError_t launch_route(const RouteParams& p, hipStream_t s, StageEvents ev = {});
+// Top-k of every row from what launch_route left (moe_route only).
+hipError_t launch_topk(const RouteParams& p, hipStream_t s);
 hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids, int32_t* union_count,
                         int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);
-hipError_t launch_gateup(const SweepParams& p, int rows, int max_slots, hipStream_t s);
-hipError_t launch_down(const SweepParams& p, int rows, int max_union, hipStream_t s);
+hipError_t launch_gateup(const SweepParams& p, int rows, int max_slots, hipStream_t s, StageEvents ev = {});
+hipError_t launch_down(const SweepParams& p, hipStream_t s, StageEvents ev = {});
+// Down sweep and blend in one kernel for few rows: the rows of output each
+// block owns when this call can run it (every pair's act fits in LDS), else 0.
+int down_blend_rows_per_block(int rows, int k, int h, int imax);
+hipError_t launch_down_blend(const SweepParams& p, int rows, int nr, hipStream_t s, StageEvents ev = {});
 // out = bf16(sum_j w*y + gamma*s); with partial non-null, partial = sum_j w*y
 // (fp32, slots mapped to -1 skipped) and out is not written.
 hipError_t launch_blend(const float* y, const float* w, const int32_t* slot_to_union, const float* gamma,
-                        uint16_t* out, float* partial, int rows, int h, int k, hipStream_t s);
+                        uint16_t* out, float* partial, int rows, int h, int k, hipStream_t s, StageEvents ev = {});
 hipError_t launch_union_local(const int32_t* ids, int rows, int k, int lo, int hi, int32_t* union_ids,
                               int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);
 // Streaming-read probe over ``bytes`` (a multiple of 16) of ``src``; writes
 // one word per block to sink[0 .. blocks).
 hipError_t launch_read_probe(const uint8_t* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
 int read_probe_blocks();
+// out = bf16(reduced + gamma * shared), the shared expert's output at pair rows*k + r.
 hipError_t launch_ep_combine(const float* reduced, const float* y, const float* gamma, uint16_t* out, int rows, int h,
-                             hipStream_t s);
+                             int k, hipStream_t s);
 
 }  // namespace moe

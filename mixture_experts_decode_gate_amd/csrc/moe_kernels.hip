@@ -16,7 +16,7 @@
 // in an order that does not depend on the other rows, so a call with R rows
 // writes each row's output bytes exactly as a one-row call would.
 
-#include <stdlib.h>
+#include <hip/hip_ext.h>
 
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -24,9 +24,10 @@
 namespace moe {
 
 // ---------------------------------------------------------------- routing
-// Router GEMV, and for moe_route top-k in the same kernel.  moe_forward runs
-// the GEMV alone; every gate/up block then takes top-k, the union and the
-// slot table itself from the stored logits (see the gate/up sweep).
+// Router GEMV.  Top-k runs in the next kernel: every gate/up block takes top-k,
+// the union and the slot table itself from the stored logits (moe_forward), or
+// topk_kernel does (moe_route).  The kernel boundary makes every router
+// block's results visible to the reader without a grid-wide hand-off.
 //
 // Block e (of E+1) computes router row e for every input row (e == E is the
 // shared expert's gate vector): wave c < nkc takes the kRouterChunk-column
@@ -34,14 +35,10 @@ namespace moe {
 // and reduces in a fixed order; the chunk partials are summed in chunk order
 // and rounded once: logits[r][e] = fp32(sum), gamma[r] = fp32(sigmoid(sum)),
 // and for sigmoid routing score[r][e] = sigmoid(sum) in fp64.
-// With top-k each block then publishes its results and takes a ticket from
-// the arrival counter; the block that draws the last ticket reads every logit
-// and runs top-k (one wave per row), then resets the counter to zero for the
-// next call.
 constexpr int kRouterChunk = 512;
 constexpr int kMaxRouterChunks = MOE_MAX_DIM / kRouterChunk;
-// A wave per router chunk, and at least one per row for top-k.
-constexpr int kRouteThreads = 64 * (kMaxRouterChunks > kMaxRows ? kMaxRouterChunks : kMaxRows);
+constexpr int kRouteThreads = 64 * kMaxRouterChunks;  // a wave per router chunk
+constexpr int kTopkThreads = 64 * kMaxRows;           // a wave per row
 static_assert(MOE_MAX_EXPERTS <= 64 * 16, "top-k holds at most 16 keys per lane");
 
 // Union of the n <= 64 ids in ids_lds (slot t = r*k + j) that lie in
@@ -52,11 +49,12 @@ static_assert(MOE_MAX_EXPERTS <= 64 * 16, "top-k holds at most 16 keys per lane"
 // forward_ep.rs splits the selected ids into local and remote ones by
 // local_expert_range).  Returns the lane's union position if it is a first
 // occurrence (else -1), in *mask_out the rows that chose its id and in
-// *count_out the union size U.  The union outputs are written when
-// union_ids is not null (row_mask may be null on its own).
+// *count_out the union size U, in *eq_out the slots that hold its id (bit t).
+// The union outputs are written when union_ids is not null (row_mask may be
+// null on its own).
 __device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows, int lo, int hi, int lane,
                           int32_t* union_ids, int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask,
-                          uint32_t* mask_out, int* count_out) {
+                          uint32_t* mask_out, int* count_out, uint64_t* eq_out) {
   const int id = lane < n ? ids_lds[lane] : -1;
   const bool local = id >= lo && id < hi;
   uint64_t eq = 0;
@@ -88,6 +86,7 @@ __device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows, int lo
   }
   *mask_out = mask;
   *count_out = __popcll(bal);
+  *eq_out = eq;
   return is_first ? pos_self : -1;
 }
 
@@ -97,7 +96,7 @@ __device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows, int lo
 // Same outputs and return value as union_wave, with U = n.
 __device__ int identity_slots(const int32_t* ids_lds, int n, int k, int lane, int32_t* union_ids,
                               int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask,
-                              uint32_t* mask_out, int* count_out) {
+                              uint32_t* mask_out, int* count_out, uint64_t* eq_out) {
   const bool used = lane < n;
   const uint32_t mask = used ? 1u << (lane / k) : 0u;
   if (used) {
@@ -108,6 +107,7 @@ __device__ int identity_slots(const int32_t* ids_lds, int n, int k, int lane, in
   if (lane == 0) *union_count = n;
   *mask_out = mask;
   *count_out = n;
+  *eq_out = used ? 1ull << lane : 0ull;
   return used ? lane : -1;
 }
 
@@ -121,7 +121,8 @@ __global__ __launch_bounds__(64) void union_kernel(const int32_t* __restrict__ i
   __syncthreads();
   uint32_t mask;
   int count;
-  union_wave(s_ids, n, k, rows, lo, hi, lane, union_ids, union_count, slot_to_union, row_mask, &mask, &count);
+  uint64_t eq;
+  union_wave(s_ids, n, k, rows, lo, hi, lane, union_ids, union_count, slot_to_union, row_mask, &mask, &count, &eq);
 }
 
 // Order-preserving map of a float key to uint32 (larger float -> larger
@@ -332,11 +333,9 @@ __device__ __forceinline__ void router_dot_nvfp4(const RouteParams& p, int e, in
   }
 }
 
-template <int R, int G>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int do_topk) {
+template <int R>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
   __shared__ double part[kMaxRouterChunks][kMaxRows];
-  __shared__ __align__(16) int32_t s_ids[kMaxIds];
-  __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int h = p.h, E = p.E;
@@ -359,12 +358,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int
   __syncthreads();
   // Wave 0: lane r sums row r's chunk partials in chunk order and takes the
   // sigmoid (the gate row always; router rows for sigmoid routing), and lane
-  // 0 writes every row's results.  Without top-k that is all: the kernel that
-  // follows reads them after the kernel boundary.  With top-k, lane 0 takes a
-  // ticket with release order (its own stores become visible before the
-  // increment), and the block drawing the last ticket acquires, so its reads
-  // see every block's results.  A full fence in every block would also
-  // invalidate every L2 on each arrival, which costs far more than the GEMV.
+  // 0 writes every row's results.  The kernel that follows reads them after
+  // the kernel boundary.
   if (wave == 0) {
     double z = 0.0, sg = 0.0;
     if (lane < R) {
@@ -397,24 +392,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p, int
         }
       }
     }
-    if (do_topk && lane == 0) {
-      const uint32_t ticket = __hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = ticket == gridDim.x - 1;
-      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      s_last = last;
-    }
   }
-  if (!do_topk) return;  // the next kernel runs top-k on these results
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  if (wave < R) {
-    TopkIn<G> in;
-    topk_load<G>(p, wave, lane, in);
-    topk_select<G>(p, wave, lane, in, s_ids, p.ids_out, p.w_out);
-  }
-  // every other block has arrived: reset for the next call
-  if (threadIdx.x == 0) __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// moe_route's top-k: one block, one wave per row, on the logits and scores
+// route_kernel stored (visible across the kernel boundary).
+template <int G>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(RouteParams p) {
+  __shared__ __align__(16) int32_t s_ids[kMaxIds];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  if (wave >= p.rows) return;
+  TopkIn<G> in;
+  topk_load<G>(p, wave, lane, in);
+  topk_select<G>(p, wave, lane, in, s_ids, p.ids_out, p.w_out);
 }
 
 // ---------------------------------------------------------------- sweeps
@@ -509,8 +500,11 @@ __device__ __forceinline__ ExpertPtrs expert_ptrs(const RouteParams& rp, int ex)
   return e;
 }
 
-// Slot table entry of a routed expert.
-__device__ __forceinline__ SlotInfo slot_info(const ExpertPtrs& e, int ex, int inter, uint32_t row_mask) {
+// Slot table entry of a routed expert.  ``eq`` holds the slots t = r*k + j
+// whose id is this expert (bit t): row r's pair is r*k + j for the one j its
+// bits name (a row's ids are distinct).
+__device__ __forceinline__ SlotInfo slot_info(const ExpertPtrs& e, int ex, int inter, uint32_t row_mask, uint64_t eq,
+                                              int k) {
   SlotInfo si;
   si.gate_packed = e.p[0];
   si.gate_scales = e.p[1];
@@ -524,10 +518,17 @@ __device__ __forceinline__ SlotInfo slot_info(const ExpertPtrs& e, int ex, int i
   si.inter = inter;
   si.row_mask = row_mask;
   si.expert = ex;
+  const uint64_t kmask = k >= 64 ? ~0ull : ((1ull << k) - 1ull);
+#pragma unroll
+  for (int r = 0; r < kMaxRows; ++r) {
+    const uint64_t m = r * k < 64 ? (eq >> (r * k)) & kmask : 0ull;
+    si.pair[r] = m ? (uint8_t)(r * k + __builtin_ctzll(m)) : (uint8_t)0xFF;
+  }
   return si;
 }
 
-// Slot table entry of the shared expert (used by every row).
+// Slot table entry of the shared expert (used by every row; row r's pair is
+// rows*k + r).
 __device__ __forceinline__ SlotInfo shared_slot_info(const RouteParams& rp, uint32_t row_mask) {
   SlotInfo si;
   si.gate_packed = rp.shared_gate.packed;
@@ -542,6 +543,8 @@ __device__ __forceinline__ SlotInfo shared_slot_info(const RouteParams& rp, uint
   si.inter = rp.shared_inter;
   si.row_mask = row_mask;
   si.expert = -1;
+#pragma unroll
+  for (int r = 0; r < kMaxRows; ++r) si.pair[r] = r < rp.rows ? (uint8_t)(rp.rows * rp.k + r) : (uint8_t)0xFF;
   return si;
 }
 
@@ -680,15 +683,19 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     i = __builtin_amdgcn_readfirstlane(i);
     return (long long)blockIdx.x + (long long)i * gridDim.x;
   };
-  // What the compute needs of an item's slot, in scalar registers.
+  // What the compute needs of an item's slot, in scalar registers: the rows
+  // that use it, the per-tensor scales and each row's pair index (byte r).
+  constexpr int kPairWords = (R + 3) / 4;
   struct ItemSlot {
     uint32_t row_mask;
     float gate_scale2, up_scale2;
+    uint32_t pairw[kPairWords];
   };
   RowRegs<NCH> ga, ua, gb, ub;
   ItemSlot sa, sb;
-  int na = 0, nb = 0, slot_a = 0, slot_b = 0;
-  auto fetch = [&](int id, RowRegs<NCH>& g, RowRegs<NCH>& u, ItemSlot& si, int& n, int& slot) {
+  int na = 0, nb = 0;
+  auto fetch = [&](int id, RowRegs<NCH>& g, RowRegs<NCH>& u, ItemSlot& si, int& n) {
+    int slot;
     if (id < p.shared_inter) {
       slot = kSharedSlot;
       n = id;
@@ -702,6 +709,8 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     si.row_mask = uniform_u32(e.row_mask);
     si.gate_scale2 = uniform_f32(e.gate_scale2);
     si.up_scale2 = uniform_f32(e.up_scale2);
+#pragma unroll
+    for (int q = 0; q < kPairWords; ++q) si.pairw[q] = uniform_u32(reinterpret_cast<const uint32_t*>(e.pair)[q]);
   };
   // A first claim on a shared-expert row needs no routing: its weights are
   // requested now and arrive while the block runs top-k.  A wave whose first
@@ -712,7 +721,7 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   long long first = claim_id();
   const bool early = first < p.shared_inter;
   const int any_id = early ? (int)first : (int)(first % p.shared_inter);
-  fetch(any_id, ga, ua, sa, na, slot_a);
+  fetch(any_id, ga, ua, sa, na);
   // Nothing that reads a loaded value may be scheduled above the fetch.
   __builtin_amdgcn_sched_barrier(0);
 
@@ -744,13 +753,14 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   if (wave == 0) {
     uint32_t mask;
     int count;
-    const int pos = p.token_major
-                        ? identity_slots(s_ids, R * rp.k, rp.k, lane, s_uids, &s_union, s_s2u, s_rmask, &mask, &count)
-                        : union_wave(s_ids, R * rp.k, rp.k, R, rp.expert_lo, rp.expert_hi, lane, s_uids, &s_union,
-                                     s_s2u, s_rmask, &mask, &count);
+    uint64_t eq;
+    const int pos = p.token_major ? identity_slots(s_ids, R * rp.k, rp.k, lane, s_uids, &s_union, s_s2u, s_rmask,
+                                                   &mask, &count, &eq)
+                                  : union_wave(s_ids, R * rp.k, rp.k, R, rp.expert_lo, rp.expert_hi, lane, s_uids,
+                                               &s_union, s_s2u, s_rmask, &mask, &count, &eq);
     if (pos >= 0) {  // lane is the union entry's first slot
       const int ex = s_ids[lane];
-      s_slots[pos] = slot_info(kPtab ? s_ptab[ex] : expert_ptrs(rp, ex), ex, rp.inter, mask);
+      s_slots[pos] = slot_info(kPtab ? s_ptab[ex] : expert_ptrs(rp, ex), ex, rp.inter, mask, eq, rp.k);
     }
   }
   __syncthreads();
@@ -763,7 +773,7 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     return id < total ? (int)id : -1;
   };
 
-  auto compute = [&](const RowRegs<NCH>& g, const RowRegs<NCH>& u, const ItemSlot& si, int n, int slot) {
+  auto compute = [&](const RowRegs<NCH>& g, const RowRegs<NCH>& u, const ItemSlot& si, int n) {
     float ag[R], au[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -799,7 +809,8 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
         const float uv = gu[1] * si.up_scale2;
         if (lane == 0) {
           const float a = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-          p.act[((size_t)slot * kMaxRows + r) * p.act_stride + n] = f32_to_bf16(a);
+          const uint32_t pr = (si.pairw[r >> 2] >> (8 * (r & 3))) & 0xFFu;
+          p.act[(size_t)pr * p.act_stride + n] = f32_to_bf16(a);
         }
       }
     }
@@ -813,7 +824,7 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   // buffer past the last claim.
   RowRegs<NCH> gc, uc;
   ItemSlot sc;
-  int nc = 0, slot_c = 0;
+  int nc = 0;
   int id_a, id_b;
   if (early) {
     id_a = (int)first;  // first < Is <= total
@@ -823,7 +834,7 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     id_b = first < total ? (int)first : -1;
   }
   const bool has_work = id_a >= 0 || id_b >= 0;
-  fetch(id_b >= 0 ? id_b : any_id, gb, ub, sb, nb, slot_b);
+  fetch(id_b >= 0 ? id_b : any_id, gb, ub, sb, nb);
   // Block 0 publishes the routing results for the down sweep and the blend.
   if (publish && wave == 0) {
     const int n = R * rp.k;
@@ -853,20 +864,20 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   // not computed.
   while (true) {
     const int id_c = id_b >= 0 ? claim() : -1;
-    fetch(id_c >= 0 ? id_c : any_id, gc, uc, sc, nc, slot_c);
+    fetch(id_c >= 0 ? id_c : any_id, gc, uc, sc, nc);
     consume<NCH>(ga);
     consume<NCH>(ua);
-    if (id_a >= 0) compute(ga, ua, sa, na, slot_a);
+    if (id_a >= 0) compute(ga, ua, sa, na);
     const int id_a2 = id_c >= 0 ? claim() : -1;
-    fetch(id_a2 >= 0 ? id_a2 : any_id, ga, ua, sa, na, slot_a);
+    fetch(id_a2 >= 0 ? id_a2 : any_id, ga, ua, sa, na);
     consume<NCH>(gb);
     consume<NCH>(ub);
-    if (id_b >= 0) compute(gb, ub, sb, nb, slot_b);
+    if (id_b >= 0) compute(gb, ub, sb, nb);
     const int id_b2 = id_a2 >= 0 ? claim() : -1;
-    fetch(id_b2 >= 0 ? id_b2 : any_id, gb, ub, sb, nb, slot_b);
+    fetch(id_b2 >= 0 ? id_b2 : any_id, gb, ub, sb, nb);
     consume<NCH>(gc);
     consume<NCH>(uc);
-    if (id_c >= 0) compute(gc, uc, sc, nc, slot_c);
+    if (id_c >= 0) compute(gc, uc, sc, nc);
     if (id_a2 < 0) break;
     id_a = id_a2;
     id_b = id_b2;
@@ -879,8 +890,9 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
 // contiguous share of segments x h output rows -- at most two segments -- so
 // waves never wait for each other.  A wave holds its group's act rows in
 // registers (loaded once per segment) and loads its next batch of weight rows
-// while it computes the current batch.
-//   y[slot][r][n] = W_down[n,:] . act[slot][r][:]
+// while it computes the current batch.  For row r of union slot u, with
+// pair t the (row, expert) pair of (u, r):
+//   y[t][n] = W_down[u][n,:] . act[t][:]
 constexpr int kDownThreads = 256;
 constexpr int kDownBatch = 4;  // weight rows per prefetch batch (stored as float4s)
 constexpr int kDownBufs = 3;   // batches in the prefetch rotation
@@ -890,11 +902,10 @@ struct DownBatch {
   RowRegs<NCH> row[kDownBatch];
 };
 
-template <int R, int NCH>
+template <int NCH>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   constexpr int kGroup = kDownGroup;  // act rows held per segment (16 VGPRs each per 2048 columns)
   constexpr int kMaxSegs = kMaxDownSegs;
-  (void)R;
   __shared__ SlotInfo s_slots[kNumSlots];
   __shared__ int s_seg_slot[kMaxSegs];
   __shared__ uint32_t s_seg_rows[kMaxSegs];  // row i of the group in bits 4i..4i+3, count in bits 28..31
@@ -969,12 +980,18 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
     const int stride = (last - first) * kDownBatch;
     const int n0 = (v - first) * kDownBatch;
     if (n0 >= n_end) continue;
-    // act rows of the group (unused entries repeat the last row).  Lanes past
-    // K read the row's first columns: finite values that meet zeroed scales.
+    // Pair index of each group row (unused entries repeat the last row).
+    int prs[kGroup];
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
       const int r = (int)((rows >> (4 * (i < cnt ? i : cnt - 1))) & 0xFu);
-      const uint16_t* src = p.act + ((size_t)slot * kMaxRows + r) * p.act_stride;
+      prs[i] = uniform_int(si.pair[r]);
+    }
+    // act rows of the group.  Lanes past K read the row's first columns:
+    // finite values that meet zeroed scales.
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const uint16_t* src = p.act + (size_t)prs[i] * p.act_stride;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int col = c * kChunk + lane * 32;
@@ -1017,8 +1034,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
       for (int g = 0; g < kGroup; ++g) {
         if (g < cnt) {
           wave_sum_n<kDownBatch>(acc[g]);
-          const int r = (int)((rows >> (4 * g)) & 0xFu);
-          float* dst = p.y + ((size_t)slot * kMaxRows + r) * h + nb;
+          float* dst = p.y + (size_t)prs[g] * h + nb;
           if (lane == 0) {
 
 #pragma unroll
@@ -1072,8 +1088,286 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   }
 }
 
+// ---------------------------------------------------------------- down sweep + blend, few rows
+// With few rows the activations of every (row, expert) pair fit in LDS, and a
+// single kernel runs the down projections and the weighted sum.  Block b owns
+// output rows [b*nr, (b+1)*nr) of every union slot and of the shared expert,
+// so every term of out[r][n] is computed inside the block: the blend needs no
+// kernel of its own and the expert outputs no round trip through memory.
+//   y[t][n]   = W_down[u][n,:] . act[t][:]        (t: the pair of slot u and row r)
+//   out[r][n] = bf16( sum_{j<k} w[r][j] * y[r*k + j][n] + gamma[r] * y[rows*k + r][n] )
+// Each y value is computed exactly as down_kernel computes it (same lane
+// columns, same chunk order, same reduction, scale2 last) and the sum runs in
+// blend_kernel's order, so both paths write the same bytes; y is also written
+// to the workspace.  Work units are (slot, batch of kDownBatch output rows),
+// the shared expert's first; the block's waves claim them from an LDS counter
+// and keep two units in flight while they compute one.
+constexpr int kDbThreads = 768;  // 12 waves, one block per CU
+constexpr int kDbMaxRows = 4;    // rows served by this kernel (act of every pair in LDS)
+constexpr int kDbActPer = 12;    // act staging loads per thread (16 bytes each)
+
+template <int R, int NCH>
+__global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, int nr) {
+  static_assert(R <= kDbMaxRows, "down_blend_kernel serves at most kDbMaxRows rows");
+  extern __shared__ u32x4 s_act[];  // [P][NCH][256] act rows (swizzled), then y as floats [P][nr]
+  __shared__ SlotInfo s_slots[kNumSlots];
+  __shared__ float s_w[kMaxIds];
+  __shared__ float s_gamma[kDbMaxRows];
+  __shared__ int32_t s_local[kMaxIds];  // slot_to_union >= 0 (EP share: local expert)
+  __shared__ int s_next, s_union;
+  const RouteParams& rp = p.route;
+  const int lane = threadIdx.x & 63;
+  const int h = p.h, k = rp.k;
+  const int P = R * k + R;  // pairs
+  float* s_y = reinterpret_cast<float*>(s_act + (size_t)P * NCH * kChunkUnits);
+  const int n_begin = blockIdx.x * nr;
+  const int nbat = nr / kDownBatch;
+
+  // Prologue: the loads that do not depend on the slot table are issued
+  // first (slot table, U, weights, gates, act rows), then a shared-expert
+  // unit's weights, and each is consumed in issue order.
+  constexpr int kSlotWords = (int)(sizeof(SlotInfo) / 4);
+  constexpr int kTabPer = (kNumSlots * kSlotWords + kDbThreads - 1) / kDbThreads;
+  uint32_t tab[kTabPer];
+#pragma unroll
+  for (int q = 0; q < kTabPer; ++q) {
+    const int i = (int)threadIdx.x + q * kDbThreads;
+    tab[q] = ld_global(reinterpret_cast<const uint32_t*>(p.slots) + (i < kNumSlots * kSlotWords ? i : 0));
+  }
+  const int ucount = ld_global(p.union_count);
+  const int tw = (int)threadIdx.x < R * k ? (int)threadIdx.x : 0;
+  const float wv = ld_global(rp.w_out + tw);
+  const int s2u = ld_global(rp.slot_to_union + tw);
+  const float gv = ld_global(rp.gamma + ((int)threadIdx.x < R ? (int)threadIdx.x : 0));
+  // act rows: unit i of the staging is 16 bytes of pair t, chunk c, unit un
+  // (columns past the pair's K read a valid copy and are stored as zeros);
+  // the launcher serves this kernel only when one pass of kDbActPer loads per
+  // thread covers every unit
+  const int units = P * NCH * kChunkUnits;
+  constexpr int kActPer = kDbActPer;
+  auto act_src = [&](int i, int& dst, bool& valid) {
+    const int t = i / (NCH * kChunkUnits);
+    const int rem = i - t * NCH * kChunkUnits;
+    const int c = rem / kChunkUnits, un = rem - c * kChunkUnits;
+    const int K = t < R * k ? p.inter : p.shared_inter;
+    const int col = c * kChunk + un * 8;
+    valid = col < K;
+    dst = (t * NCH + c) * kChunkUnits + swz_unit(un);
+    return reinterpret_cast<const u32x4*>(p.act + (size_t)t * p.act_stride + (valid ? col : 0));
+  };
+  u32x4 av[kActPer];
+#pragma unroll
+  for (int q = 0; q < kActPer; ++q) {
+    const int i = (int)threadIdx.x + q * kDbThreads;
+    int dst;
+    bool valid;
+    av[q] = ld_global(act_src(i < units ? i : 0, dst, valid));
+  }
+  if (threadIdx.x == 0) {
+    s_next = 0;
+    s_slots[kSharedSlot] = shared_slot_info(rp, (1u << R) - 1u);
+  }
+  __syncthreads();
+
+  auto claim_id = [&]() -> int {
+    int i = 0;
+    if (lane == 0) i = atomicAdd(&s_next, 1);
+    return __builtin_amdgcn_readfirstlane(i);
+  };
+  // What the compute needs of a unit, in scalar registers.
+  constexpr int kPairWords = (R + 3) / 4;
+  struct UnitInfo {
+    int n, K;
+    float d2;
+    uint32_t mask;
+    uint32_t pairw[kPairWords];
+  };
+  // unit id: slot s = id / nbat (0: the shared expert, then union slot s - 1),
+  // output rows n_begin + (id % nbat) * kDownBatch + 0..3
+  auto fetch = [&](int id, DownBatch<NCH>& b, UnitInfo& ui) {
+    const int sidx = id / nbat;
+    const int slot = sidx == 0 ? kSharedSlot : sidx - 1;
+    const int n = n_begin + (id - sidx * nbat) * kDownBatch;
+    const SlotInfo& e = s_slots[slot];
+    const uint8_t* const dp = uniform_ptr(e.down_packed);
+    const uint8_t* const ds = uniform_ptr(e.down_scales);
+    const int K = uniform_int(e.inter);
+#pragma unroll
+    for (int i = 0; i < kDownBatch; ++i) load_row<NCH>(b.row[i], dp, ds, n + i < h ? n + i : h - 1, K, lane);
+    ui.n = n;
+    ui.K = K;
+    ui.d2 = uniform_f32(e.down_scale2);
+    ui.mask = uniform_u32(e.row_mask);
+#pragma unroll
+    for (int q = 0; q < kPairWords; ++q) ui.pairw[q] = uniform_u32(reinterpret_cast<const uint32_t*>(e.pair)[q]);
+  };
+  // Shared-expert units need no slot table: the first claim is fetched now
+  // when it is one; otherwise a shared unit stands in (loaded, not computed).
+  // That stand-in also serves every unit past the last claim.
+  const int first = claim_id();
+  const bool early = first < nbat;
+  const int any_id = early ? first : 0;
+  DownBatch<NCH> ba, bb, bc;
+  UnitInfo ia, ib, ic;
+  fetch(any_id, ba, ia);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Consume, in issue order: the slot table, U, weights and gates, act rows.
+  {
+#pragma unroll
+    for (int q = 0; q < kTabPer; ++q) {
+      const int i = (int)threadIdx.x + q * kDbThreads;
+      // the shared slot's entry is this call's (set above); every other is the gate/up sweep's
+      if (i < kNumSlots * kSlotWords && i / kSlotWords != kSharedSlot)
+        reinterpret_cast<uint32_t*>(s_slots)[i] = tab[q];
+    }
+    if (threadIdx.x == 0) s_union = ucount;
+    if ((int)threadIdx.x < R * k) {
+      s_w[threadIdx.x] = wv;
+      s_local[threadIdx.x] = s2u >= 0;
+    }
+    if ((int)threadIdx.x < R) s_gamma[threadIdx.x] = gv;
+#pragma unroll
+    for (int q = 0; q < kActPer; ++q) {
+      const int i = (int)threadIdx.x + q * kDbThreads;
+      if (i < units) {
+        int dst;
+        bool valid;
+        act_src(i, dst, valid);
+        s_act[dst] = valid ? av[q] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kTabPer; ++q) asm volatile("" ::"v"(tab[q]));
+#pragma unroll
+    for (int q = 0; q < kActPer; ++q) asm volatile("" ::"v"(av[q]));
+  }
+  __syncthreads();
+  const int total = (s_union + 1) * nbat;
+  auto claim = [&]() -> int {
+    const int id = claim_id();
+    return id < total ? id : -1;
+  };
+
+  // Rows of a unit in groups of two (act rows from LDS), each weight row
+  // decoded once per group; y to LDS and the workspace.
+  auto compute = [&](const DownBatch<NCH>& b, const UnitInfo& ui) {
+#pragma unroll
+    for (int g = 0; g < (R + 1) / 2; ++g) {
+      const int r0 = 2 * g, r1 = 2 * g + 1;
+      const bool u0 = (ui.mask >> r0) & 1u;
+      const bool u1 = r1 < R && ((ui.mask >> r1) & 1u);
+      if (!u0 && !u1) continue;
+      const int p0 = (int)((ui.pairw[r0 >> 2] >> (8 * (r0 & 3))) & 0xFFu);
+      const int p1 = r1 < R ? (int)((ui.pairw[r1 >> 2] >> (8 * (r1 & 3))) & 0xFFu) : p0;
+      u32x4 x0[NCH][4], x1[NCH][4];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const u32x4* a0 = s_act + (p0 * NCH + c) * kChunkUnits;
+        const u32x4* a1 = s_act + ((u1 ? p1 : p0) * NCH + c) * kChunkUnits;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          x0[c][q] = a0[q * 64 + lane];
+          x1[c][q] = a1[q * 64 + lane];
+        }
+      }
+      float acc0[kDownBatch], acc1[kDownBatch];
+#pragma unroll
+      for (int i = 0; i < kDownBatch; ++i) {
+        acc0[i] = 0.f;
+        acc1[i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          bf16x2 dw[16];
+          decode32(b.row[i].q[c], dw);
+          const uint32_t sc = scale_pair<NCH>(b.row[i], c, ui.K, lane);
+          const float s0 = e4m3<0>(sc), s1 = e4m3<1>(sc);
+          if (u0) acc0[i] = dot32(dw, x0[c][0], x0[c][1], x0[c][2], x0[c][3], s0, s1, acc0[i]);
+          if (u1) acc1[i] = dot32(dw, x1[c][0], x1[c][1], x1[c][2], x1[c][3], s0, s1, acc1[i]);
+        }
+      }
+      auto emit = [&](float (&acc)[kDownBatch], int pr) {
+        wave_sum_n<kDownBatch>(acc);
+        if (lane == 0) {
+          const int nl = ui.n - n_begin;
+          float* dst = p.y + (size_t)pr * h + ui.n;
+          if (ui.n + kDownBatch <= h) {
+            *reinterpret_cast<float4*>(dst) =
+                make_float4(acc[0] * ui.d2, acc[1] * ui.d2, acc[2] * ui.d2, acc[3] * ui.d2);
+          } else {
+#pragma unroll
+            for (int i = 0; i < kDownBatch; ++i)
+              if (ui.n + i < h) dst[i] = acc[i] * ui.d2;
+          }
+#pragma unroll
+          for (int i = 0; i < kDownBatch; ++i) s_y[pr * nr + nl + i] = acc[i] * ui.d2;
+        }
+      };
+      if (u0) emit(acc0, p0);
+      if (u1) emit(acc1, p1);
+    }
+  };
+
+  int id_a, id_b;
+  if (early) {
+    id_a = first;  // < nbat <= total
+    id_b = claim();
+  } else {
+    id_a = -1;
+    id_b = first < total ? first : -1;
+  }
+  if (id_a >= 0 || id_b >= 0) {
+    fetch(id_b >= 0 ? id_b : any_id, bb, ib);
+    // One exit, after a whole rotation (see the gate/up sweep).
+    while (true) {
+      const int id_c = id_b >= 0 ? claim() : -1;
+      fetch(id_c >= 0 ? id_c : any_id, bc, ic);
+#pragma unroll
+      for (int q = 0; q < kDownBatch; ++q) consume<NCH>(ba.row[q]);
+      if (id_a >= 0) compute(ba, ia);
+      const int id_a2 = id_c >= 0 ? claim() : -1;
+      fetch(id_a2 >= 0 ? id_a2 : any_id, ba, ia);
+#pragma unroll
+      for (int q = 0; q < kDownBatch; ++q) consume<NCH>(bb.row[q]);
+      if (id_b >= 0) compute(bb, ib);
+      const int id_b2 = id_a2 >= 0 ? claim() : -1;
+      fetch(id_b2 >= 0 ? id_b2 : any_id, bb, ib);
+#pragma unroll
+      for (int q = 0; q < kDownBatch; ++q) consume<NCH>(bc.row[q]);
+      if (id_c >= 0) compute(bc, ic);
+      if (id_a2 < 0) break;
+      id_a = id_a2;
+      id_b = id_b2;
+    }
+#pragma unroll
+    for (int q = 0; q < kDownBatch; ++q) {
+      consume<NCH>(ba.row[q]);
+      consume<NCH>(bb.row[q]);
+    }
+  }
+  __syncthreads();
+
+  // The weighted sum of the block's rows, in blend_kernel's order.
+  const int t = (int)threadIdx.x;
+  if (t < R * nr) {
+    const int r = t / nr, i = t - (t / nr) * nr;
+    const int n = n_begin + i;
+    if (n < h) {
+      float acc = 0.f;
+      for (int j = 0; j < k; ++j)
+        if (p.partial == nullptr || s_local[r * k + j]) acc = __builtin_fmaf(s_w[r * k + j], s_y[(r * k + j) * nr + i], acc);
+      if (p.partial != nullptr) {
+        p.partial[(size_t)r * h + n] = acc;
+      } else {
+        acc = __builtin_fmaf(s_gamma[r], s_y[(R * k + r) * nr + i], acc);
+        p.out[(size_t)r * h + n] = f32_to_bf16(acc);
+      }
+    }
+  }
+}
+
 // Weighted sum and shared-expert blend, one thread per (row, column):
-//   out[r][n] = bf16( sum_{j<k} w[r][j] * y[slot(r,j)][r][n] + gamma[r] * y[shared][r][n] )
+//   out[r][n] = bf16( sum_{j<k} w[r][j] * y[r*k + j][n] + gamma[r] * y[rows*k + r][n] )
 // summed in fp32 in ascending j.  With partial non-null (one rank's share
 // under expert parallelism) it writes the routed sum alone, in fp32, over the
 // slots whose expert is local (slot_to_union >= 0): forward_token_major.rs
@@ -1081,31 +1375,30 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
 __global__ __launch_bounds__(256) void blend_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                     const int32_t* __restrict__ slot_to_union,
                                                     const float* __restrict__ gamma, uint16_t* __restrict__ out,
-                                                    float* __restrict__ partial, int h, int k) {
+                                                    float* __restrict__ partial, int h, int k, int rows) {
   constexpr int kB = 8;  // slots whose loads are issued together
   const int r = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= h) return;
-  // The shared term's loads go out with the first batch; each batch issues
-  // all its slot-index and weight loads, then all its y loads, then adds in
-  // ascending j: a few memory round trips per thread instead of one per slot.
+  // Outputs are stored by pair, so no load waits for another: each batch of
+  // eight slots issues its weight and output loads together, then adds in
+  // ascending j.
   const float g = gamma[r];
-  const float ys = y[((size_t)kSharedSlot * kMaxRows + r) * h + n];
+  const float ys = y[(size_t)(rows * k + r) * h + n];
   float acc = 0.f;
   for (int j0 = 0; j0 < k; j0 += kB) {
-    int sl[kB];
     float wv[kB], yv[kB];
+    bool use[kB];
 #pragma unroll
     for (int q = 0; q < kB; ++q) {
       const int j = j0 + q < k ? j0 + q : k - 1;
-      sl[q] = j0 + q < k ? slot_to_union[r * k + j] : -1;
       wv[q] = w[r * k + j];
+      yv[q] = y[(size_t)(r * k + j) * h + n];
+      use[q] = j0 + q < k && (partial == nullptr || slot_to_union[r * k + j] >= 0);
     }
 #pragma unroll
-    for (int q = 0; q < kB; ++q) yv[q] = y[((size_t)(sl[q] >= 0 ? sl[q] : 0) * kMaxRows + r) * h + n];
-#pragma unroll
     for (int q = 0; q < kB; ++q)
-      if (sl[q] >= 0) acc = __builtin_fmaf(wv[q], yv[q], acc);
+      if (use[q]) acc = __builtin_fmaf(wv[q], yv[q], acc);
   }
   if (partial != nullptr) {
     partial[(size_t)r * h + n] = acc;
@@ -1118,16 +1411,15 @@ __global__ __launch_bounds__(256) void blend_kernel(const float* __restrict__ y,
 // The shared expert added after the all-reduce of the ranks' partials
 // (forward_token_major.rs: moe_batched_blend, or residual_add when the gate
 // weight is null, where gamma = 1):
-//   out[r][n] = bf16( reduced[r][n] + gamma[r] * y[shared][r][n] )
+//   out[r][n] = bf16( reduced[r][n] + gamma[r] * y[rows*k + r][n] )
 __global__ __launch_bounds__(256) void ep_combine_kernel(const float* __restrict__ reduced,
                                                          const float* __restrict__ y,
                                                          const float* __restrict__ gamma,
-                                                         uint16_t* __restrict__ out, int h) {
+                                                         uint16_t* __restrict__ out, int h, int k, int rows) {
   const int r = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= h) return;
-  const float acc =
-      __builtin_fmaf(gamma[r], y[((size_t)kSharedSlot * kMaxRows + r) * h + n], reduced[(size_t)r * h + n]);
+  const float acc = __builtin_fmaf(gamma[r], y[(size_t)(rows * k + r) * h + n], reduced[(size_t)r * h + n]);
   out[(size_t)r * h + n] = f32_to_bf16(acc);
 }
 
@@ -1173,6 +1465,15 @@ namespace {
 // served without caching.
 constexpr int kMaxDevices = 64;
 
+// Launch shapes, measured on MI355X: the gate/up sweep runs 8 waves per CU
+// (one 512-thread block: its staged x and 196 VGPRs allow no more), the down
+// sweep 12 (three 256-thread blocks), the read probe 16 blocks per CU with 16
+// loads in flight per lane (the fastest of 4 / 8 / 16 each).
+constexpr int kGateupWavesPerCU = 8;
+constexpr int kDownWavesPerCU = 12;
+constexpr int kProbeBlocksPerCU = 16;
+constexpr int kProbeUnroll = 16;
+
 int current_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
@@ -1190,54 +1491,47 @@ int cu_count() {
   return n;
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  const int x = atoi(v);
-  return x > 0 ? x : dflt;
-}
-
-// Sweep launch shape: threads per block and blocks per CU.  Blocks per CU is
-// the occupancy limit (queried once per kernel instance) capped so a CU runs
-// about 8 waves; MOE_WAVES_PER_CU overrides that for tuning runs.
-struct SweepShape {
-  int threads = 0;
-  int per_cu = 0;
+template <class T>
+struct no_deduce {
+  using type = T;
 };
 
-// ``caches`` is the calling kernel instance's per-device array of launch shapes.
-template <typename K>
-dim3 sweep_grid(K kernel, size_t lds, int max_blocks, SweepShape (&caches)[kMaxDevices], int default_threads) {
-  const int dev = current_device();
-  SweepShape local;
-  SweepShape& cache = (dev >= 0 && dev < kMaxDevices) ? caches[dev] : local;
-  if (cache.threads <= 0) {
-    const int threads = default_threads;
-    const int waves_per_cu = env_int("MOE_WAVES_PER_CU", 8);
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu <= 0)
-      per_cu = 1;
-    const int want = (waves_per_cu * 64 + threads - 1) / threads;
-    cache.threads = threads;
-    cache.per_cu = per_cu < want ? per_cu : (want < 1 ? 1 : want);
+// Launch ``kernel``; with stage events, through hipExtLaunchKernel so the
+// events record the kernel's own start and end.
+template <typename... KArgs>
+hipError_t launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s, StageEvents ev,
+                    typename no_deduce<KArgs>::type... args) {
+  if (ev.start != nullptr || ev.stop != nullptr) {
+    void* argv[] = {static_cast<void*>(&args)...};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, s, ev.start, ev.stop, 0);
   }
-  int grid = cu_count() * cache.per_cu;
-  if (grid > max_blocks) grid = max_blocks;
-  return dim3(grid < 1 ? 1 : grid);
-}
-
-template <int R>
-hipError_t route_r(const RouteParams& p, bool do_topk, hipStream_t s) {
-  // keys per lane: 4 covers up to 256 experts, 16 up to MOE_MAX_EXPERTS
-  if (p.E <= 256)
-    hipLaunchKernelGGL((route_kernel<R, 4>), dim3(p.E + 1), dim3(kRouteThreads), 0, s, p, (int)do_topk);
-  else
-    hipLaunchKernelGGL((route_kernel<R, 16>), dim3(p.E + 1), dim3(kRouteThreads), 0, s, p, (int)do_topk);
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
   return hipGetLastError();
 }
 
+// Blocks per CU for a sweep kernel: the occupancy limit (queried once per
+// kernel instance and device), capped at ``waves_per_cu`` waves.
+template <typename K>
+int blocks_per_cu(K kernel, int threads, size_t lds, int waves_per_cu, int (&cache)[kMaxDevices]) {
+  const int dev = current_device();
+  int local = 0;
+  int& per_cu = (dev >= 0 && dev < kMaxDevices) ? cache[dev] : local;
+  if (per_cu <= 0) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, lds) != hipSuccess || occ <= 0) occ = 1;
+    const int want = (waves_per_cu * 64 + threads - 1) / threads;
+    per_cu = occ < want ? occ : (want < 1 ? 1 : want);
+  }
+  return per_cu;
+}
+
+template <int R>
+hipError_t route_r(const RouteParams& p, hipStream_t s, StageEvents ev) {
+  return launch_k(route_kernel<R>, dim3(p.E + 1), dim3(kRouteThreads), 0, s, ev, p);
+}
+
 template <int R, int NCH, int G>
-hipError_t gateup_rng(const SweepParams& p, int max_items, hipStream_t s) {
+hipError_t gateup_rng(const SweepParams& p, int max_items, hipStream_t s, StageEvents ev) {
   const size_t lds = (size_t)R * NCH * kChunkUnits * 16;
   // The dynamic LDS limit is set once per device (the attribute is per device).
   static bool attr_set[kMaxDevices] = {false};
@@ -1248,69 +1542,78 @@ hipError_t gateup_rng(const SweepParams& p, int max_items, hipStream_t s) {
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
   }
-  static SweepShape shapes[kMaxDevices];
-  const dim3 grid = sweep_grid(gateup_kernel<R, NCH, G>, lds, 1 << 30, shapes, kMaxSweepThreads);
-  const int threads = kMaxSweepThreads;
-  const int waves = (int)grid.x * (threads / 64);
-  dim3 g = grid;
-  if (waves > max_items) g.x = (max_items * 64 + threads - 1) / threads;
-  hipLaunchKernelGGL((gateup_kernel<R, NCH, G>), g, dim3(threads), lds, s, p);
-  return hipGetLastError();
+  static int per_cu[kMaxDevices] = {0};
+  constexpr int threads = kMaxSweepThreads;
+  int grid = cu_count() * blocks_per_cu(gateup_kernel<R, NCH, G>, threads, lds, kGateupWavesPerCU, per_cu);
+  // no more waves than work items
+  if (grid * (threads / 64) > max_items) grid = (max_items * 64 + threads - 1) / threads;
+  return launch_k(gateup_kernel<R, NCH, G>, dim3(grid < 1 ? 1 : grid), dim3(threads), lds, s, ev, p);
 }
 
 template <int R, int NCH>
-hipError_t gateup_rn(const SweepParams& p, int max_items, hipStream_t s) {
+hipError_t gateup_rn(const SweepParams& p, int max_items, hipStream_t s, StageEvents ev) {
   // top-k keys per lane: 4 covers up to 256 experts, 16 up to MOE_MAX_EXPERTS
-  return p.route.E <= 256 ? gateup_rng<R, NCH, 4>(p, max_items, s) : gateup_rng<R, NCH, 16>(p, max_items, s);
+  return p.route.E <= 256 ? gateup_rng<R, NCH, 4>(p, max_items, s, ev) : gateup_rng<R, NCH, 16>(p, max_items, s, ev);
 }
 
-template <int R, int NCH>
-hipError_t down_rn(const SweepParams& p, int max_union, hipStream_t s) {
-  static int per_cu_dev[kMaxDevices] = {0};
+template <int NCH>
+hipError_t down_n(const SweepParams& p, hipStream_t s, StageEvents ev) {
+  static int per_cu[kMaxDevices] = {0};
+  const int grid = cu_count() * blocks_per_cu(down_kernel<NCH>, kDownThreads, 0, kDownWavesPerCU, per_cu);
+  return launch_k(down_kernel<NCH>, dim3(grid), dim3(kDownThreads), 0, s, ev, p);
+}
+
+// LDS the few-row down+blend kernel needs beyond its static arrays: every
+// pair's act row padded to whole 2048-column chunks, and the block's y values.
+size_t down_blend_dyn_lds(int rows, int k, int nr) {
+  const size_t P = (size_t)rows * k + rows;
+  return P * kChunkUnits * 16 + P * (size_t)nr * sizeof(float);
+}
+
+int max_lds_per_block() {
+  static int cached[kMaxDevices] = {0};
   const int dev = current_device();
-  int local = 0;
-  int& per_cu = (dev >= 0 && dev < kMaxDevices) ? per_cu_dev[dev] : local;
-  if (per_cu <= 0) {
-    int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, down_kernel<R, NCH>, kDownThreads, 0) != hipSuccess ||
-        occ <= 0)
-      occ = 1;
-    const int want = env_int("MOE_DOWN_WAVES_PER_CU", 12) / (kDownThreads / 64);
-    per_cu = occ < want ? occ : (want < 1 ? 1 : want);
-  }
-  const int grid = cu_count() * per_cu;
-  (void)max_union;
-  hipLaunchKernelGGL((down_kernel<R, NCH>), dim3(grid), dim3(kDownThreads), 0, s, p);
-  return hipGetLastError();
+  if (dev >= 0 && dev < kMaxDevices && cached[dev]) return cached[dev];
+  int v = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+    v = 64 * 1024;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev] = v;
+  return v;
 }
 
 template <int R>
-hipError_t gateup_r(const SweepParams& p, int nch, int max_tiles, hipStream_t s) {
-  switch (nch) {
-    case 1: return gateup_rn<R, 1>(p, max_tiles, s);
-    case 2: return gateup_rn<R, 2>(p, max_tiles, s);
-    case 3: return gateup_rn<R, 3>(p, max_tiles, s);
-    case 4: return gateup_rn<R, 4>(p, max_tiles, s);
+hipError_t down_blend_r(const SweepParams& p, int nr, hipStream_t s, StageEvents ev) {
+  const size_t lds = down_blend_dyn_lds(R, p.route.k, nr);
+  static size_t attr_set[kMaxDevices] = {0};  // dynamic LDS limit set so far, per device
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxDevices || attr_set[dev] < lds) {
+    const hipError_t e = hipFuncSetAttribute((const void*)down_blend_kernel<R, 1>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = lds;
   }
-  return hipErrorInvalidValue;
+  const int grid = (p.h + nr - 1) / nr;
+  return launch_k(down_blend_kernel<R, 1>, dim3(grid), dim3(kDbThreads), lds, s, ev, p, nr);
 }
 
 template <int R>
-hipError_t down_r(const SweepParams& p, int nch, int max_union, hipStream_t s) {
+hipError_t gateup_r(const SweepParams& p, int nch, int max_items, hipStream_t s, StageEvents ev) {
   switch (nch) {
-    case 1: return down_rn<R, 1>(p, max_union, s);
-    case 2: return down_rn<R, 2>(p, max_union, s);
+    case 1: return gateup_rn<R, 1>(p, max_items, s, ev);
+    case 2: return gateup_rn<R, 2>(p, max_items, s, ev);
+    case 3: return gateup_rn<R, 3>(p, max_items, s, ev);
+    case 4: return gateup_rn<R, 4>(p, max_items, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_route(const RouteParams& p, bool do_topk, hipStream_t s) {
+hipError_t launch_route(const RouteParams& p, hipStream_t s, StageEvents ev) {
   switch (p.rows) {
 #define MOE_ROUTE_CASE(R) \
   case R:                 \
-    return route_r<R>(p, do_topk, s);
+    return route_r<R>(p, s, ev);
     MOE_ROUTE_CASE(1)
     MOE_ROUTE_CASE(2)
     MOE_ROUTE_CASE(3)
@@ -1324,81 +1627,90 @@ hipError_t launch_route(const RouteParams& p, bool do_topk, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_topk(const RouteParams& p, hipStream_t s) {
+  // keys per lane: 4 covers up to 256 experts, 16 up to MOE_MAX_EXPERTS
+  if (p.E <= 256) return launch_k(topk_kernel<4>, dim3(1), dim3(kTopkThreads), 0, s, StageEvents{}, p);
+  return launch_k(topk_kernel<16>, dim3(1), dim3(kTopkThreads), 0, s, StageEvents{}, p);
+}
+
 hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids, int32_t* union_count,
                         int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s) {
-  hipLaunchKernelGGL(union_kernel, dim3(1), dim3(64), 0, s, ids, rows, k, 0, MOE_MAX_EXPERTS, union_ids,
-                     union_count, slot_to_union, row_mask);
-  return hipGetLastError();
+  return launch_k(union_kernel, dim3(1), dim3(64), 0, s, StageEvents{}, ids, rows, k, 0, (int)MOE_MAX_EXPERTS,
+                  union_ids, union_count, slot_to_union, row_mask);
 }
 
 hipError_t launch_union_local(const int32_t* ids, int rows, int k, int lo, int hi, int32_t* union_ids,
                               int32_t* union_count, int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s) {
-  hipLaunchKernelGGL(union_kernel, dim3(1), dim3(64), 0, s, ids, rows, k, lo, hi, union_ids, union_count,
-                     slot_to_union, row_mask);
-  return hipGetLastError();
+  return launch_k(union_kernel, dim3(1), dim3(64), 0, s, StageEvents{}, ids, rows, k, lo, hi, union_ids, union_count,
+                  slot_to_union, row_mask);
 }
 
-hipError_t launch_gateup(const SweepParams& p, int rows, int max_slots, hipStream_t s) {
+hipError_t launch_gateup(const SweepParams& p, int rows, int max_slots, hipStream_t s, StageEvents ev) {
   const int nch = (p.h + kChunk - 1) / kChunk;
-  const int max_tiles = max_slots * p.inter + p.shared_inter;  // work items (rows)
+  const int max_items = max_slots * p.inter + p.shared_inter;  // work items (weight rows)
   switch (rows) {
-    case 1: return gateup_r<1>(p, nch, max_tiles, s);
-    case 2: return gateup_r<2>(p, nch, max_tiles, s);
-    case 3: return gateup_r<3>(p, nch, max_tiles, s);
-    case 4: return gateup_r<4>(p, nch, max_tiles, s);
-    case 5: return gateup_r<5>(p, nch, max_tiles, s);
-    case 6: return gateup_r<6>(p, nch, max_tiles, s);
-    case 7: return gateup_r<7>(p, nch, max_tiles, s);
-    case 8: return gateup_r<8>(p, nch, max_tiles, s);
+    case 1: return gateup_r<1>(p, nch, max_items, s, ev);
+    case 2: return gateup_r<2>(p, nch, max_items, s, ev);
+    case 3: return gateup_r<3>(p, nch, max_items, s, ev);
+    case 4: return gateup_r<4>(p, nch, max_items, s, ev);
+    case 5: return gateup_r<5>(p, nch, max_items, s, ev);
+    case 6: return gateup_r<6>(p, nch, max_items, s, ev);
+    case 7: return gateup_r<7>(p, nch, max_items, s, ev);
+    case 8: return gateup_r<8>(p, nch, max_items, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_down(const SweepParams& p, int rows, int max_union, hipStream_t s) {
+hipError_t launch_down(const SweepParams& p, hipStream_t s, StageEvents ev) {
   const int kmax = p.inter > p.shared_inter ? p.inter : p.shared_inter;
-  const int nch = (kmax + kChunk - 1) / kChunk;
-  const int max_tiles = max_union;  // down_rn derives its tile count from the union bound
+  switch ((kmax + kChunk - 1) / kChunk) {
+    case 1: return down_n<1>(p, s, ev);
+    case 2: return down_n<2>(p, s, ev);
+  }
+  return hipErrorInvalidValue;
+}
+
+int down_blend_rows_per_block(int rows, int k, int h, int imax) {
+  if (rows < 1 || rows > kDbMaxRows || imax > kChunk) return 0;
+  const int P = rows * k + rows;
+  if (P * kChunkUnits > kDbActPer * kDbThreads) return 0;  // one staging pass
+  // one block per CU, a whole number of batches per block
+  const int per = (h + cu_count() - 1) / cu_count();
+  const int nr = (per + kDownBatch - 1) / kDownBatch * kDownBatch;
+  hipFuncAttributes fa;
+  if (hipFuncGetAttributes(&fa, (const void*)down_blend_kernel<kDbMaxRows, 1>) != hipSuccess) return 0;
+  if (fa.sharedSizeBytes + down_blend_dyn_lds(rows, k, nr) > (size_t)max_lds_per_block()) return 0;
+  return nr;
+}
+
+hipError_t launch_down_blend(const SweepParams& p, int rows, int nr, hipStream_t s, StageEvents ev) {
   switch (rows) {
-    case 1: return down_r<1>(p, nch, max_tiles, s);
-    case 2: return down_r<2>(p, nch, max_tiles, s);
-    case 3: return down_r<3>(p, nch, max_tiles, s);
-    case 4: return down_r<4>(p, nch, max_tiles, s);
-    case 5: return down_r<5>(p, nch, max_tiles, s);
-    case 6: return down_r<6>(p, nch, max_tiles, s);
-    case 7: return down_r<7>(p, nch, max_tiles, s);
-    case 8: return down_r<8>(p, nch, max_tiles, s);
+    case 1: return down_blend_r<1>(p, nr, s, ev);
+    case 2: return down_blend_r<2>(p, nr, s, ev);
+    case 3: return down_blend_r<3>(p, nr, s, ev);
+    case 4: return down_blend_r<4>(p, nr, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_blend(const float* y, const float* w, const int32_t* slot_to_union, const float* gamma,
-                        uint16_t* out, float* partial, int rows, int h, int k, hipStream_t s) {
-  dim3 grid((h + 255) / 256, rows);
-  hipLaunchKernelGGL(blend_kernel, grid, dim3(256), 0, s, y, w, slot_to_union, gamma, out, partial, h, k);
-  return hipGetLastError();
+                        uint16_t* out, float* partial, int rows, int h, int k, hipStream_t s, StageEvents ev) {
+  return launch_k(blend_kernel, dim3((h + 255) / 256, rows), dim3(256), 0, s, ev, y, w, slot_to_union, gamma, out,
+                  partial, h, k, rows);
 }
 
 hipError_t launch_ep_combine(const float* reduced, const float* y, const float* gamma, uint16_t* out, int rows, int h,
-                             hipStream_t s) {
-  dim3 grid((h + 255) / 256, rows);
-  hipLaunchKernelGGL(ep_combine_kernel, grid, dim3(256), 0, s, reduced, y, gamma, out, h);
-  return hipGetLastError();
+                             int k, hipStream_t s) {
+  return launch_k(ep_combine_kernel, dim3((h + 255) / 256, rows), dim3(256), 0, s, StageEvents{}, reduced, y, gamma,
+                  out, h, k, rows);
 }
 
 hipError_t launch_read_probe(const uint8_t* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s) {
-  // Loads in flight per lane: 16 by default (the fastest of 4 / 8 / 16 measured
-  // on MI355X); MOE_PROBE_UNROLL overrides it for tuning runs.
-  switch (env_int("MOE_PROBE_UNROLL", 16)) {
-    case 4: hipLaunchKernelGGL(read_probe_kernel<4>, dim3(blocks), dim3(kProbeThreads), 0, s, src, bytes / 16, sink); break;
-    case 8: hipLaunchKernelGGL(read_probe_kernel<8>, dim3(blocks), dim3(kProbeThreads), 0, s, src, bytes / 16, sink); break;
-    default: hipLaunchKernelGGL(read_probe_kernel<16>, dim3(blocks), dim3(kProbeThreads), 0, s, src, bytes / 16, sink);
-  }
-  return hipGetLastError();
+  return launch_k(read_probe_kernel<kProbeUnroll>, dim3(blocks), dim3(kProbeThreads), 0, s, StageEvents{}, src,
+                  bytes / 16, sink);
 }
 
-// 16 blocks per CU (half of them queued behind the resident ones) measured
-// fastest of 4 / 8 / 16; MOE_PROBE_BLOCKS_PER_CU overrides it for tuning runs.
-int read_probe_blocks() { return cu_count() * env_int("MOE_PROBE_BLOCKS_PER_CU", 16); }
+int read_probe_blocks() { return cu_count() * kProbeBlocksPerCU; }
 
 }  // namespace moe
 

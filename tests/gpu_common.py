@@ -35,10 +35,12 @@ def x_dev(bits: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).cuda()
 
 
-def ws_for(cfg):
+def ws_for(cfg, fill: int = 0xFF):
+    """A workspace of moe_workspace_bytes(cfg), filled with ``fill``: the
+    library reads nothing it has not written in the same call."""
     torch = torch_cuda()
     moe = moe_mod()
-    return torch.zeros(moe.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    return torch.full((moe.moe_workspace_bytes(cfg),), fill, dtype=torch.uint8, device="cuda")
 
 
 def ws_read(ws, offset: int, dtype, count: int) -> np.ndarray:
@@ -62,8 +64,6 @@ def run_forward(dl, x_bits: np.ndarray, ws=None):
     ws = ws_for(dl.cfg) if ws is None else ws
     moe.moe_forward(dl.cfg, dl.weights, x, out, ws)
     torch.cuda.synchronize()
-    # the routing kernel's arrival counter is back at zero after every call
-    assert ws_read(ws, moe.moe_workspace_layout(dl.cfg).sync, np.uint32, 1)[0] == 0
     return out_bits(out), ws
 
 

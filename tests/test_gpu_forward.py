@@ -21,6 +21,8 @@ import synth
 from oracle.formats import E4M3FN_TABLE, dequant_nvfp4, f32_to_bf16_bits
 from oracle.layer import moe_layer_from
 from oracle.ffn import silu
+from oracle.route import selection_keys, topk_margin
+from oracle.union import expert_union
 
 from gpu_common import (REL_L2_TOL, REL_MAX_TOL, W_RTOL, bits_to_f64, moe_mod, out_bits, output_errors,
                         run_forward, torch_cuda, upload, ws_for, ws_read, x_dev)
@@ -29,10 +31,14 @@ pytestmark = pytest.mark.gpu
 
 
 def read_intermediates(dl, ws, rows):
+    """Routing, union and the per-pair activations and expert outputs the call
+    left in the workspace (pair r*k + j: row r's j-th expert; rows*k + r: row
+    r's shared expert)."""
     moe = moe_mod()
     L = moe.moe_workspace_layout(dl.cfg)
     k, h = dl.cfg.top_k, dl.cfg.hidden
     imax = max(dl.cfg.moe_inter, dl.cfg.shared_inter)
+    P = rows * (k + 1)
     U = int(ws_read(ws, L.union_count, np.int32, 1)[0])
     return dict(
         ids=ws_read(ws, L.topk_ids, np.int32, 8 * k).reshape(8, k)[:rows],
@@ -42,35 +48,64 @@ def read_intermediates(dl, ws, rows):
         union_ids=ws_read(ws, L.union_ids, np.int32, 64)[:U],
         slot_to_union=ws_read(ws, L.slot_to_union, np.int32, rows * k),
         row_mask=ws_read(ws, L.row_mask, np.uint32, 64)[:U],
-        act=ws_read(ws, L.act, np.uint16, 65 * 8 * imax).reshape(65, 8, imax),
-        y=ws_read(ws, L.y, np.float32, 65 * 8 * h).reshape(65, 8, h),
+        act=ws_read(ws, L.act, np.uint16, P * imax).reshape(P, imax),
+        y=ws_read(ws, L.y, np.float32, P * h).reshape(P, h),
     )
 
 
+# A row whose k-th and (k+1)-th selection keys lie closer than this is a
+# near-tie: an independent evaluation of the logits may pick either expert.
+NEAR_TIE = 1e-5
+
+
+def near_tie_rows(weights, ref):
+    """Per-row k/(k+1) key margins of the oracle's keys; rows below NEAR_TIE
+    are reported in the test output.  Seeds are never changed to avoid them."""
+    s = weights.shape
+    keys = selection_keys(ref["logits"], weights.bias, s.route_kind)
+    margins = np.array([topk_margin(keys[r], s.top_k) for r in range(keys.shape[0])])
+    near = np.nonzero(margins < NEAR_TIE)[0]
+    if near.size:
+        print(f"near-tie rows {near.tolist()} (k/(k+1) key margins {margins[near].tolist()})")
+    return keys, near
+
+
 def check_against_oracle(weights, dl, x_bits, rows_checked=None):
-    R = x_bits.shape[0]
+    R, k = x_bits.shape[0], dl.cfg.top_k
     got, ws = run_forward(dl, x_bits)
     ref = moe_layer_from(weights, x_bits, rows=rows_checked)
     mid = read_intermediates(dl, ws, R)
-    assert np.array_equal(mid["ids"], ref["ids"])
-    np.testing.assert_allclose(mid["weights"], ref["weights"], rtol=W_RTOL, atol=0)
-    assert mid["union_count"] == ref["union_count"]
-    assert np.array_equal(mid["union_ids"], ref["union_ids"])
-    assert np.array_equal(mid["slot_to_union"], ref["slot_to_union"])
-    assert np.array_equal(mid["row_mask"], ref["row_mask"])
-    rows = ref["rows"]
+    keys, near = near_tie_rows(weights, ref)
+    same = np.array([np.array_equal(mid["ids"][r], ref["ids"][r]) for r in range(R)])
+    for r in range(R):
+        if r in near and not same[r]:
+            # a near-tie decided the other way: the GPU's ids must still be a
+            # top-k of the oracle's keys, within the near-tie margin
+            gk = np.sort(keys[r][mid["ids"][r]].astype(np.float64))[::-1]
+            rk = np.sort(keys[r].astype(np.float64))[::-1][:k]
+            assert len(set(mid["ids"][r].tolist())) == k and np.all(np.abs(gk - rk) <= NEAR_TIE), r
+            print(f"row {r}: near-tie decided differently; its weights and outputs are not compared")
+        else:
+            assert same[r], (r, mid["ids"][r], ref["ids"][r])
+            np.testing.assert_allclose(mid["weights"][r], ref["weights"][r], rtol=W_RTOL, atol=0)
+    # the union of the ids the GPU selected (the oracle's, but for a near-tie row decided the other way)
+    u_ids, U, s2u, mask = expert_union(mid["ids"])
+    assert mid["union_count"] == U
+    assert np.array_equal(mid["union_ids"], u_ids)
+    assert np.array_equal(mid["slot_to_union"], s2u)
+    assert np.array_equal(mid["row_mask"], mask)
+    rows = [r for r in ref["rows"] if same[r]]
     rel_l2, rel_max = output_errors(got[rows], ref["out"][rows])
     assert np.all(rel_l2 <= REL_L2_TOL), rel_l2
     assert np.all(rel_max <= REL_MAX_TOL), rel_max
-    # expert outputs y per (row, slot) and the shared expert
+    # expert outputs per (row, expert) pair and the shared expert
     for r in rows:
-        for j in range(dl.cfg.top_k):
-            u = ref["slot_to_union"][r * dl.cfg.top_k + j]
+        for j in range(k):
             yr = ref["y"][r, j].astype(np.float64)
-            yg = mid["y"][u, r].astype(np.float64)
+            yg = mid["y"][r * k + j].astype(np.float64)
             assert np.linalg.norm(yg - yr) <= 1e-2 * np.linalg.norm(yr)
         sr = ref["shared_y"][r].astype(np.float64)
-        assert np.linalg.norm(mid["y"][64, r] - sr) <= 1e-2 * np.linalg.norm(sr)
+        assert np.linalg.norm(mid["y"][R * k + r] - sr) <= 1e-2 * np.linalg.norm(sr)
     return got, ref, rel_l2
 
 
@@ -101,10 +136,10 @@ def test_forward_c3_verify4_full(layer256):
     check_against_oracle(w3, dl, synth.activations(shape, 0))
 
 
-def test_forward_c4_prefill8_sampled_rows(layer256):
+def test_forward_c4_prefill8_all_rows(layer256):
     weights, dl = layer256
     shape = synth.CONFIGS["c4_e256_prefill8"]
-    check_against_oracle(weights, dl, synth.activations(shape, 0), rows_checked=[0, 7])
+    check_against_oracle(weights, dl, synth.activations(shape, 0))
 
 
 def test_rows_equal_one_row_calls_256(layer256):
@@ -155,25 +190,27 @@ def test_stages_with_every_scale_byte():
     got, ws = run_forward(dl, x)
     mid = read_intermediates(dl, ws, shape.rows)
     xf = bits_to_f64(x)
-    U = mid["union_count"]
-    slots = list(range(U)) + [64]
+    U, R, k = mid["union_count"], shape.rows, shape.top_k
+    slots = list(range(U)) + [-1]
     for u in slots:
-        if u == 64:
+        if u < 0:
             g, up, dn = weights.shared
-            mask = (1 << shape.rows) - 1
+            mask = (1 << R) - 1
         else:
             e = int(mid["union_ids"][u])
             g, up, dn = (weights.expert(e, p) for p in range(3))
             mask = int(mid["row_mask"][u])
         Wg, Wu, Wd = (dequant_nvfp4(t.packed, t.scales, t.scale2, t.n, t.k) for t in (g, up, dn))
-        for r in range(shape.rows):
+        for r in range(R):
             if not (mask >> r) & 1:
                 continue
+            # the (row, expert) pair that holds this slot's activations and output for row r
+            t = R * k + r if u < 0 else r * k + mid["ids"][r].tolist().index(e)
             # gate/up: act = bf16(silu(g) * v) from float64 dot products
             gd, vd = Wg @ xf[r], Wu @ xf[r]
             gb = np.abs(Wg) @ np.abs(xf[r])
             vb = np.abs(Wu) @ np.abs(xf[r])
-            act_g = bits_to_f64(mid["act"][u, r, :g.n])
+            act_g = bits_to_f64(mid["act"][t, :g.n])
             a_ref = silu(gd) * vd
             # bound: fp32 sums (relative 4e-6 of the absolute sums) propagated through silu(g)*v,
             # plus one bf16 rounding of the result
@@ -183,7 +220,7 @@ def test_stages_with_every_scale_byte():
             # down: from the kernel's own bf16 activations
             yd = Wd @ act_g
             yb = np.abs(Wd) @ np.abs(act_g)
-            y_g = mid["y"][u, r].astype(np.float64)
+            y_g = mid["y"][t].astype(np.float64)
             assert np.all(np.abs(y_g - yd) <= 4e-6 * yb + 1e-30), (u, r)
     ref = moe_layer_from(weights, x)
     rel_l2, rel_max = output_errors(got, ref["out"])
@@ -410,7 +447,7 @@ def test_ep_shares_256(layer256):
     shape = synth.CONFIGS["c4_e256_prefill8"]
     x = synth.activations(shape, 0)
     ranges = [(32 * g, 32 * (g + 1)) for g in range(8)]
-    check_ep_shares(weights, dl, x, ranges, rows_checked=[0, 7])
+    check_ep_shares(weights, dl, x, ranges)
 
 
 @pytest.mark.parametrize("name", ["c0_tiny", "c2_e128_verify2"])
@@ -437,6 +474,32 @@ def test_forward_nvfp4_router(name):
     x = synth.activations(shape, 1)
     check_against_oracle(weights, dl, x)
     check_token_major(dl, x)
+
+
+# ---------------------------------------------------------------- more than 256 experts
+# Past 256 experts the gate/up sweep keeps 16 top-k keys per lane and reads
+# each union slot's weight pointers from the expert tables instead of an LDS
+# copy of every expert's pointers.
+WIDE_E = [
+    synth.MoeShape("e512_sigmoid", 512, 512, 8, 64, 64, 8, synth.ROUTE_SIGMOID_BIAS, True, 2.5),
+    synth.MoeShape("e1024_softmax", 512, 1024, 8, 64, 64, 8, synth.ROUTE_SOFTMAX, True, 1.0),
+    synth.MoeShape("e1024_sigmoid", 512, 1024, 8, 64, 96, 8, synth.ROUTE_SIGMOID_BIAS, True, 2.5),
+    synth.MoeShape("e300_softmax_nonorm", 256, 300, 6, 96, 64, 5, synth.ROUTE_SOFTMAX, False, 1.0),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE_E, ids=[s.name for s in WIDE_E])
+def test_forward_more_than_256_experts(shape):
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = synth.activations(shape, 0)
+    check_against_oracle(weights, dl, x)
+    singles = np.stack([run_forward(dl, x[r:r + 1])[0][0] for r in range(shape.rows)])
+    got, _ = run_forward(dl, x)
+    assert np.array_equal(got, singles)
+    check_token_major(dl, x)
+    E = shape.num_experts
+    check_ep_shares(weights, dl, x, [(0, E // 3), (E // 3, E - 1), (E - 1, E)])
 
 
 # ---------------------------------------------------------------- maximum sizes
@@ -644,16 +707,21 @@ def test_forward_timed_matches_forward_and_times_every_stage():
     want, _ = run_forward(dl, x_bits)
     x = x_dev(x_bits)
     n = moe.moe_num_stages()
-    assert moe.moe_stage_names() == ["route", "gate_up_sweep", "down_sweep", "blend"]
-    for events in ([HipEvent() for _ in range(n + 1)], [None] * (n + 1), [HipEvent(), None, HipEvent(), None, None]):
+    names = moe.moe_stage_names()
+    assert names[0] == "route" and names[1] == "gate_up_sweep" and len(names) == n
+    some = [HipEvent() if i % 3 == 0 else None for i in range(2 * n)]
+    for events in ([HipEvent() for _ in range(2 * n)], [None] * (2 * n), some):
         out = torch.zeros_like(x)
         moe.moe_forward_timed(dl.cfg, dl.weights, x, out, ws_for(dl.cfg), events)
         torch.cuda.synchronize()
         assert np.array_equal(out_bits(out), want)
-    ev = [HipEvent() for _ in range(n + 1)]
+    ev = [HipEvent() for _ in range(2 * n)]
     out = torch.zeros_like(x)
     moe.moe_forward_timed(dl.cfg, dl.weights, x, out, ws_for(dl.cfg), ev)
     torch.cuda.synchronize()
-    stages = [ev[i].elapsed_ms(ev[i + 1]) for i in range(n)]
-    assert all(t >= 0.0 for t in stages) and stages[1] > 0.0
-    assert abs(sum(stages) - ev[0].elapsed_ms(ev[n])) <= 1e-3 + 1e-3 * ev[0].elapsed_ms(ev[n])
+    # each stage's kernel runs between its own start and stop, in stage order
+    stages = [ev[2 * i].elapsed_ms(ev[2 * i + 1]) for i in range(n)]
+    gaps = [ev[2 * i + 1].elapsed_ms(ev[2 * i + 2]) for i in range(n - 1)]
+    assert all(t > 0.0 for t in stages), stages
+    assert all(g >= 0.0 for g in gaps), gaps
+    assert sum(stages) <= ev[0].elapsed_ms(ev[2 * n - 1]) * (1 + 1e-3) + 1e-3
