@@ -89,7 +89,8 @@ enum {
   MOE_MAX_EXPERTS = 1024,     /* design cap on num_experts                       */
   MOE_MAX_DIM = 8192,         /* cap on hidden                                   */
   MOE_MAX_INTER = 4096,       /* cap on moe_inter and shared_inter               */
-  MOE_DIM_ALIGN = 32          /* hidden, moe_inter, shared_inter multiple of 32  */
+  MOE_DIM_ALIGN = 32,         /* hidden, moe_inter, shared_inter multiple of 32  */
+  MOE_STATIC_SCRATCH_BYTES = 8 << 20 /* moe_forward_static's workspace, per GPU   */
 };
 
 /* Layer configuration (Glm5NextMlpConfig subset used by the routed path). */
@@ -218,6 +219,20 @@ moe_status moe_union_local(const int32_t* topk_ids, int32_t rows, int32_t top_k,
  * same bytes as a one-row call with that row. */
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                        uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * workspace is the library's own array of MOE_STATIC_SCRATCH_BYTES in each
+ * GPU's memory, held from the first call on that GPU until the process ends.
+ * Nothing else differs from moe_forward: same arguments (no workspace),
+ * refusals and output bytes.  The call allocates nothing.  Refused with
+ * MOE_ERR_UNSUPPORTED, before any HIP call, when moe_workspace_bytes(cfg)
+ * exceeds MOE_STATIC_SCRATCH_BYTES.  Every call on one GPU shares that GPU's
+ * array, which keeps the last call's intermediates: calls that overlap in
+ * time on one GPU (other streams, other threads) race and give undefined
+ * results; order them on one stream. */
+moe_status moe_forward_static(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
+                              uint16_t* out_bf16, int32_t rows, void* stream);
 
 /* The layer over any number of rows, in sub-chunks of min(MOE_MAX_ROWS,
  * MOE_MAX_IDS / top_k) consecutive rows, each one moe_forward on ``stream``

@@ -8,6 +8,7 @@ libmoe.so.  The names match the C ABI in include/moe.h:
     moe_route(cfg, w, x, topk_ids, topk_w, ws)       router + top-k
     moe_union(topk_ids, union_ids, union_count, slot_to_union, row_mask, num_experts)
     moe_forward(cfg, w, x, out, ws)                  the whole layer
+    moe_forward_static(cfg, w, x, out)               the whole layer, library-held workspace (no allocation)
     moe_forward_token_major(cfg, w, x, out, ws)      the layer without the union (one slot per pair)
     moe_forward_prefill(cfg, w, x, out, ws)          any number of rows, in 8-row sub-chunks
     moe_forward_timed(cfg, w, x, out, ws, events)    same, with per-stage events
@@ -33,6 +34,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID_BIAS = 0, 1
 MOE_MAX_ROWS, MOE_MAX_IDS, MOE_MAX_EXPERTS, MOE_MAX_DIM, MOE_MAX_INTER = 8, 64, 1024, 8192, 4096
+MOE_STATIC_SCRATCH_BYTES = 8 << 20
 # Expert activations and outputs in the workspace are stored by (row, expert)
 # pair: pair r*k + j is row r's j-th routed expert, rows*k + r row r's shared expert.
 MAX_PAIRS = MOE_MAX_IDS + MOE_MAX_ROWS
@@ -110,6 +112,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward.argtypes = [P(MoeConfig), P(MoeWeights), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
                                 C.c_size_t, C.c_void_p]
     lib.moe_forward.restype = C.c_int
+    lib.moe_forward_static.argtypes = [P(MoeConfig), P(MoeWeights), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]
+    lib.moe_forward_static.restype = C.c_int
     lib.moe_forward_prefill.argtypes = lib.moe_forward.argtypes
     lib.moe_forward_prefill.restype = C.c_int
     lib.moe_forward_token_major.argtypes = lib.moe_forward.argtypes
@@ -184,6 +188,12 @@ def moe_forward(cfg: MoeConfig, w: MoeWeights, x, out, ws, stream=None) -> None:
     """x [rows, h] bf16 -> out [rows, h] bf16 (device tensors); ws a uint8 device tensor."""
     _check(load().moe_forward(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(x.shape[0]), _ptr(ws),
                               int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def moe_forward_static(cfg: MoeConfig, w: MoeWeights, x, out, stream=None) -> None:
+    """moe_forward with the library's own per-GPU workspace: allocates nothing."""
+    _check(load().moe_forward_static(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(x.shape[0]),
+                                     _stream(stream)))
 
 
 def moe_forward_prefill(cfg: MoeConfig, w: MoeWeights, x, out, ws, stream=None) -> None:

@@ -10,9 +10,17 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
+
+// Workspace of moe_forward_static: one array per GPU, in the library's own
+// device memory, held until the process ends.  In host code ``scratch`` names a
+// host-side stand-in, not a device address: the address each GPU holds it at
+// comes from hipGetSymbolAddress (scratch_address below) and only that address
+// is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -209,6 +217,30 @@ moe_status check_union_args(const int32_t* topk_ids, int32_t rows, int32_t top_k
 
 moe_status device_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+// Device address of ``scratch`` on the current device, looked up once per
+// device with that device current (each GPU holds its own copy).
+constexpr int kScratchDevices = 64;
+struct ScratchAddress {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchAddress g_scratch[kScratchDevices];
+
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d: the static workspace serves devices 0..%d", dev, kScratchDevices - 1);
+  ScratchAddress& s = g_scratch[dev];
+  std::call_once(s.once, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+  if (s.err != hipSuccess) return device_status(s.err, "hipGetSymbolAddress(scratch)");
+  if (!s.ptr) return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+  *out = s.ptr;
   return MOE_OK;
 }
 
@@ -418,6 +450,29 @@ moe_status moe_union_local(const int32_t* topk_ids, int32_t rows, int32_t top_k,
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16, uint16_t* out_bf16,
                        int32_t rows, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, ws_bytes, stream, nullptr, ForwardMode());
+}
+
+moe_status moe_forward_static(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16, uint16_t* out_bf16,
+                              int32_t rows, void* stream) {
+  // Every refusal before any HIP call, as moe_forward's: the layout of this
+  // config must fit the static workspace.
+  moe_status st = check_config(cfg);
+  if (st) return st;
+  if ((st = check_rows(cfg, rows))) return st;
+  moe_ws_layout L;
+  compute_layout(cfg, &L);
+  if (L.total > (size_t)MOE_STATIC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED, "the layer's workspace needs %zu bytes; the static workspace holds %d",
+                L.total, (int)MOE_STATIC_SCRATCH_BYTES);
+  if ((st = check_all_weights(cfg, w))) return st;
+  if (!x_bf16 || !aligned(x_bf16, 16)) return fail(MOE_ERR_INVALID_ARG, "x must be a 16-byte aligned device pointer");
+  if (!out_bf16 || !aligned(out_bf16, 16)) return fail(MOE_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  const size_t xb = (size_t)rows * cfg->hidden * sizeof(uint16_t);
+  if (overlaps(x_bf16, xb, out_bf16, xb)) return fail(MOE_ERR_INVALID_ARG, "x and out overlap");
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return forward_impl(cfg, w, x_bf16, out_bf16, rows, ws, (size_t)MOE_STATIC_SCRATCH_BYTES, stream, nullptr,
+                      ForwardMode());
 }
 
 moe_status moe_forward_prefill(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,

@@ -265,3 +265,25 @@ def test_prefill_refusals():
     w = fake_weights()
     w.router_w = BASE + 0x1004
     assert pf(40, w=w) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_static_forward_refusals():
+    """moe_forward_static refuses bad arguments as moe_forward does, before any HIP call."""
+    cfg = cfg_c4()
+    st = lambda rows=4, x=X, out=OUT, w=None, c=cfg: lib.moe_forward_static(
+        ctypes.byref(c), ctypes.byref(w or fake_weights()), x, out, rows, None)
+    assert st(rows=0) == moe.MOE_ERR_INVALID_ARG
+    assert st(rows=9) == moe.MOE_ERR_INVALID_ARG
+    assert st(x=0) == moe.MOE_ERR_INVALID_ARG
+    assert st(out=0) == moe.MOE_ERR_INVALID_ARG
+    assert st(x=X + 2) == moe.MOE_ERR_INVALID_ARG                # misaligned
+    assert st(out=X + 6144 * 2) == moe.MOE_ERR_INVALID_ARG       # out overlaps x
+    assert st(c=cfg_c4(hidden=100)) == moe.MOE_ERR_INVALID_ARG
+    w = fake_weights()
+    w.router_w = BASE + 0x1004
+    assert st(w=w) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_static(ctypes.byref(cfg), None, X, OUT, 4, None) == moe.MOE_ERR_INVALID_ARG
+    # the workspace of every configuration the caps allow fits the static array
+    big = moe.MoeConfig(moe.MOE_MAX_DIM, moe.MOE_MAX_EXPERTS, moe.MOE_MAX_IDS, moe.MOE_MAX_INTER, moe.MOE_MAX_INTER,
+                        moe.MOE_ROUTE_SIGMOID_BIAS, 1, 2.5)
+    assert 0 < lib.moe_workspace_bytes(ctypes.byref(big)) <= moe.MOE_STATIC_SCRATCH_BYTES
