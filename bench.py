@@ -127,6 +127,23 @@ def union_sizes(cfg, layers, xs, ws):
     return us
 
 
+def settle(cfg, layers, xs, ws, ms):
+    """Untimed steps for ``ms`` milliseconds of host time, back to back.  After
+    the setup (weight upload, one step per input with a host read-back each),
+    the first few tens of steps run about 5% slower than the steady state
+    while the device's clocks settle; a timed region of 20 steps started then
+    would measure the transition, not the layer."""
+    import torch
+    import mixture_experts_decode_gate_amd as moe
+    out = torch.empty_like(xs[0])
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < ms / 1e3:
+        moe.moe_forward(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], out, ws)
+        i += 1
+    torch.cuda.synchronize()
+    return i
+
+
 def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, stage_events=False, token_major=False):
     """K back-to-back steps between two events on the launch stream.  With
     stage_events, every step is launched through moe_forward_timed, whose
@@ -179,6 +196,56 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, stage_events=
                                bytes_per_launch=b / len(traced), launches=len(traced))
         res["stages"] = stage
     return res
+
+
+def union_vs_subchunks(cfg, layers, shape, K, steps, ws, sub_rows=8):
+    """K rows as one moe_forward (one union over all K rows' experts) against
+    the same rows as sub-chunks of ``sub_rows`` rows, one moe_forward each
+    (each sub-chunk dedups only its own experts).  Same inputs, same layer
+    copies; µs per K rows and the experts each form streams."""
+    import torch
+    import mixture_experts_decode_gate_amd as moe
+    import synth
+    from mixture_experts_decode_gate_amd.hip_events import HipEvent
+    L = moe.moe_workspace_layout(cfg)
+    xs = [torch.from_numpy(synth.activations(shape, s, rows=K).view(np.int16)).cuda() for s in range(N_INPUTS)]
+    out = torch.empty_like(xs[0])
+    chunks = [(r0, min(K, r0 + sub_rows)) for r0 in range(0, K, sub_rows)]
+
+    def u_of():
+        torch.cuda.synchronize()
+        return int(ws[L.union_count:L.union_count + 4].cpu().numpy().view(np.int32)[0])
+    u_one, u_sub = [], []
+    for i, x in enumerate(xs):
+        moe.moe_forward(cfg, layers[i % len(layers)].weights, x, out, ws)
+        u_one.append(u_of())
+        tot = 0
+        for a, b in chunks:
+            moe.moe_forward(cfg, layers[i % len(layers)].weights, x[a:b], out[a:b], ws)
+            tot += u_of()
+        u_sub.append(tot)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for mode in ("one_union", "sub_chunks"):
+        torch.cuda.synchronize()
+        for i in range(10):  # warm-up, back to back with the timed steps
+            moe.moe_forward(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], out, ws)
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(sh)
+        for i in range(steps):
+            lay, x = layers[i % len(layers)], xs[i % len(xs)]
+            if mode == "one_union":
+                moe.moe_forward(cfg, lay.weights, x, out, ws)
+            else:
+                for a, b in chunks:
+                    moe.moe_forward(cfg, lay.weights, x[a:b], out[a:b], ws)
+        e1.record(sh)
+        torch.cuda.synchronize()
+        res[mode] = e0.elapsed_ms(e1) * 1e3 / steps
+    return dict(workload=shape.name, rows=K, sub_chunk_rows=sub_rows, experts_one_union=float(np.mean(u_one)),
+                experts_sub_chunks=float(np.mean(u_sub)), one_union_us=round(res["one_union"], 2),
+                sub_chunks_us=round(res["sub_chunks"], 2), speedup=round(res["sub_chunks"] / res["one_union"], 4),
+                expert_streams_saved=round(1 - np.mean(u_one) / np.mean(u_sub), 4))
 
 
 def config_runs(steps, main_shape, main_layers, main_cfg, ws_main):
@@ -365,6 +432,10 @@ def main():
     ap.add_argument("--layers", type=int, default=8, help="device copies of the layer cycled by the steps")
     ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=40.0,
+                    help="untimed steps before the first timed region, in host milliseconds")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="configuration of the headline run (profiling other configurations)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for rocprofv3: no sweep, no CPU leg")
     ap.add_argument("--copy-calib", action="store_true", help="only run the plain copy kernel (PMC calibration)")
@@ -390,7 +461,7 @@ def main():
     if args.profile:
         args.no_sweep, args.no_cpu = True, True
 
-    base_shape = synth.CONFIGS[WORKLOAD]
+    base_shape = synth.CONFIGS[args.workload]
     shape = base_shape.with_rows(args.rows) if args.rows != base_shape.rows else base_shape
     cfg, layers = build_layers(base_shape, args.layers)
     ws = torch.zeros(moe.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
@@ -402,6 +473,8 @@ def main():
     xs = inputs(args.rows)
     us = union_sizes(cfg, layers, xs, ws)
     log(f"[bench] unions over {N_INPUTS} inputs: {us}")
+    settle_steps = settle(cfg, layers, xs, ws, args.settle_ms)
+    log(f"[bench] {settle_steps} untimed settle steps ({args.settle_ms:.0f} ms)")
     res = timed_run(cfg, layers, xs, us, shape, args.rows, args.steps, args.warmup, ws)
     log(f"[bench] rows={args.rows}: {res['us_per_step']:.1f} us/step, {res['gbps']:.0f} GB/s")
     # the same K steps again, every kernel with its own start and stop events
@@ -437,6 +510,25 @@ def main():
                            expert_streams_saved=round(1 - a["mean_union"] / (R * shp.top_k), 4)))
             log(f"[bench] A/B rows={R} ({kind}): union {a['us_per_step']:.1f} us (U={a['mean_union']:.2f}) vs "
                 f"token-major {b['us_per_step']:.1f} us ({R * shp.top_k} streams): x{ab[-1]['speedup']:.3f}")
+
+    # More than 8 rows in one call (the union over two 64-slot tiles) against
+    # the pages' 8-row sub-chunks, on correlated verify rows: K = 12 at the
+    # 256-expert shape (hidden 6144 stages at most 12 rows of x), K = 12 and 16
+    # at the 128-expert shape (hidden 4096).
+    wide = []
+    if not args.no_sweep:
+        c3 = synth.CONFIGS["c3_e256_verify4"]
+        wide.append(union_vs_subchunks(cfg, layers, c3.with_rows(12), 12, args.sweep_steps, ws))
+        log(f"[bench] rows>8: {wide[-1]}")
+        c2 = synth.CONFIGS["c2_e128_verify2"]
+        per_step = step_bytes(c2, 16, 16 * c2.top_k)["layer"]
+        cfg2, layers2 = build_layers(c2, int(min(16, max(2, -(-(1 << 30) // per_step)))))
+        ws2 = torch.zeros(moe.moe_workspace_bytes(cfg2), dtype=torch.uint8, device="cuda")
+        for K in (12, 16):
+            wide.append(union_vs_subchunks(cfg2, layers2, c2.with_rows(K), K, args.sweep_steps, ws2))
+            log(f"[bench] rows>8: {wide[-1]}")
+        del layers2, ws2
+        torch.cuda.empty_cache()
 
     configs = config_runs(args.sweep_steps, base_shape, layers, cfg, ws) if not args.no_sweep else []
 
@@ -477,9 +569,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{WORKLOAD}: h=6144 E=256 top_k=8 I=Is=2048 rows={args.rows} "
-                               "sigmoid+bias rsf=2.5 NVFP4 experts, independent N(0,1) rows",
+        "config": {"workload": f"{base_shape.name}: h={base_shape.hidden} E={base_shape.num_experts} "
+                               f"top_k={base_shape.top_k} I={base_shape.moe_inter} Is={base_shape.shared_inter} "
+                               f"rows={args.rows} "
+                               + ("sigmoid+bias rsf=%g" % base_shape.routed_scaling_factor
+                                  if base_shape.route_kind == synth.ROUTE_SIGMOID_BIAS else "softmax")
+                               + f" NVFP4 experts, {base_shape.x_kind} rows",
                    "rows": args.rows, "layer_copies": args.layers, "inputs": N_INPUTS,
+                   "settle_steps": settle_steps,
                    "mean_union": res["mean_union"]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(st["gbps"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(st["gbps"] / HBM_PEAK_GBPS, 4),
@@ -495,6 +592,7 @@ def main():
         "pct_of_read_ceiling": round(100 * res["gbps"] / read_gbps, 2),
         "sweep": sweep,
         "union_vs_token_major": ab,
+        "union_past_8_rows_vs_8_row_sub_chunks": wide,
         "configs": configs,
         "ep_share": ep,
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},

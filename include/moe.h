@@ -1,6 +1,6 @@
 /*
  * moe.h -- C ABI of the routed mixture-of-experts layer for small-row decode
- * and speculative-verify steps (rows = 1..8), built for AMD Instinct MI355X
+ * and speculative-verify steps (rows = 1..16), built for AMD Instinct MI355X
  * (gfx950) as libmoe.so.
  *
  * What is computed (sources are cited by page title and section):
@@ -84,8 +84,11 @@ typedef enum moe_status {
 enum {
   MOE_ROUTE_SOFTMAX = 0,      /* softmax top-k, optional renormalisation        */
   MOE_ROUTE_SIGMOID_BIAS = 1, /* sigmoid + correction bias, routed_scaling_factor */
-  MOE_MAX_ROWS = 8,           /* rows per call ("WIDENED (2026-08-31)" note)     */
-  MOE_MAX_IDS = 64,           /* top_k * rows ("RETRACTED (2026-08-29)" note)    */
+  MOE_MAX_ROWS = 16,          /* rows per call (MOE_BLOCK_IDS ids in one wave tile) */
+  MOE_MAX_IDS = 128,          /* top_k * rows, two tiles of MOE_BLOCK_IDS         */
+  MOE_BLOCK_IDS = 64,         /* the one-block union of the "RETRACTED (2026-08-29)"
+                                 and "WIDENED (2026-08-31)" notes: 8 rows x 8    */
+  MOE_MAX_CHUNK_ROWS = 36,    /* rows * ceil(hidden / 2048) a call stages in LDS */
   MOE_MAX_EXPERTS = 1024,     /* design cap on num_experts                       */
   MOE_MAX_DIM = 8192,         /* cap on hidden                                   */
   MOE_MAX_INTER = 4096,       /* cap on moe_inter and shared_inter               */
@@ -191,6 +194,10 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t
 
 /* Union of the experts selected by ``rows`` rows ("Function forward_moe"
  * rustdoc, "RETRACTED (2026-08-29)" note: one block, pairwise scan, no sort).
+ * Up to MOE_BLOCK_IDS ids this is that one-block union; up to MOE_MAX_IDS the
+ * same scan runs over two tiles of MOE_BLOCK_IDS slots and the second tile's
+ * union positions continue the first's (the order stays first occurrence in
+ * row-major slot order).
  *   topk_ids       [rows, top_k] int32 in, each row's ids distinct, in [0, num_experts)
  *   union_ids      [MOE_MAX_IDS] out, first occurrence in row-major slot order
  *   union_count    [1] out, U
@@ -216,7 +223,10 @@ moe_status moe_union_local(const int32_t* topk_ids, int32_t rows, int32_t top_k,
  * accumulated).  x and out 16-byte aligned and not overlapping.  Leaves every
  * intermediate of moe_ws_layout in the workspace.  Each row's output depends
  * on that row's input alone: a call with R rows writes, for every row, the
- * same bytes as a one-row call with that row. */
+ * same bytes as a one-row call with that row.  rows <= MOE_MAX_ROWS with
+ * top_k * rows <= MOE_MAX_IDS; rows * ceil(hidden / 2048) > MOE_MAX_CHUNK_ROWS
+ * is refused with MOE_ERR_UNSUPPORTED (the sweep keeps every row of x in LDS;
+ * moe_forward_prefill serves longer batches). */
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                        uint16_t* out_bf16, int32_t rows, void* ws, size_t ws_bytes, void* stream);
 
@@ -234,8 +244,10 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const uint16
 moe_status moe_forward_static(const moe_config* cfg, const moe_weights* w, const uint16_t* x_bf16,
                               uint16_t* out_bf16, int32_t rows, void* stream);
 
-/* The layer over any number of rows, in sub-chunks of min(MOE_MAX_ROWS,
- * MOE_MAX_IDS / top_k) consecutive rows, each one moe_forward on ``stream``
+/* The layer over any number of rows, in sub-chunks of the most rows one
+ * moe_forward call takes for cfg (min(MOE_MAX_ROWS, MOE_MAX_IDS / top_k,
+ * MOE_MAX_CHUNK_ROWS / ceil(hidden / 2048))) consecutive rows, each one
+ * moe_forward on ``stream``
  * with ``ws``, in row order ("Function forward_moe" rustdoc, "WIDENED
  * (2026-08-31)" note: the 8-row batched prefill sub-chunk amortises its
  * routed experts over its own union).  x[rows, h] in, out[rows, h] out; rows

@@ -33,7 +33,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID_BIAS = 0, 1
-MOE_MAX_ROWS, MOE_MAX_IDS, MOE_MAX_EXPERTS, MOE_MAX_DIM, MOE_MAX_INTER = 8, 64, 1024, 8192, 4096
+MOE_MAX_ROWS, MOE_MAX_IDS, MOE_MAX_EXPERTS, MOE_MAX_DIM, MOE_MAX_INTER = 16, 128, 1024, 8192, 4096
+MOE_BLOCK_IDS, MOE_MAX_CHUNK_ROWS = 64, 36
 MOE_STATIC_SCRATCH_BYTES = 8 << 20
 # Expert activations and outputs in the workspace are stored by (row, expert)
 # pair: pair r*k + j is row r's j-th routed expert, rows*k + r row r's shared expert.

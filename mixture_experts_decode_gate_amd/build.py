@@ -21,7 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_abi.hip", "moe_kernels.hip"]
+SOURCES = ["moe_abi.hip", "moe_kernels.hip", "moe_gateup_rows_1_4.hip", "moe_gateup_rows_5_8.hip",
+           "moe_gateup_rows_9_12.hip", "moe_gateup_rows_13_16.hip"]
 ARCH = "gfx950"
 
 

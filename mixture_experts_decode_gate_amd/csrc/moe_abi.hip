@@ -81,12 +81,30 @@ moe_status check_config(const moe_config* c) {
   return MOE_OK;
 }
 
+// Column chunks of 2048 the gate/up sweep stages per row of x.
+int x_chunks(const moe_config* c) { return (c->hidden + 2047) / 2048; }
+
+// Largest rows one call serves for this config: MOE_MAX_ROWS, top_k * rows
+// <= MOE_MAX_IDS, and rows * x_chunks <= MOE_MAX_CHUNK_ROWS (the gate/up
+// sweep holds every row of x in LDS).
+int max_rows(const moe_config* c) {
+  int r = MOE_MAX_ROWS;
+  if (MOE_MAX_IDS / c->top_k < r) r = MOE_MAX_IDS / c->top_k;
+  if (MOE_MAX_CHUNK_ROWS / x_chunks(c) < r) r = MOE_MAX_CHUNK_ROWS / x_chunks(c);
+  return r;
+}
+
 moe_status check_rows(const moe_config* c, int32_t rows) {
   if (rows < 1 || rows > MOE_MAX_ROWS)
     return fail(MOE_ERR_INVALID_ARG, "rows=%d outside [1, %d]", rows, MOE_MAX_ROWS);
   if (c->top_k * rows > MOE_MAX_IDS)
-    return fail(MOE_ERR_INVALID_ARG, "top_k*rows=%d exceeds the %d ids one block deduplicates", c->top_k * rows,
+    return fail(MOE_ERR_INVALID_ARG, "top_k*rows=%d exceeds the %d ids the union takes", c->top_k * rows,
                 MOE_MAX_IDS);
+  if (rows * x_chunks(c) > MOE_MAX_CHUNK_ROWS)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "rows=%d at hidden=%d stages %d chunks of x in LDS (at most %d): at most %d rows per call here; "
+                "moe_forward_prefill takes any number",
+                rows, c->hidden, rows * x_chunks(c), MOE_MAX_CHUNK_ROWS, MOE_MAX_CHUNK_ROWS / x_chunks(c));
   return MOE_OK;
 }
 
@@ -161,7 +179,7 @@ void compute_layout(const moe_config* c, moe_ws_layout* L) {
   L->union_count = take(sizeof(int32_t));
   L->slot_to_union = take(MOE_MAX_IDS * sizeof(int32_t));
   L->row_mask = take(MOE_MAX_IDS * sizeof(uint32_t));
-  L->slot_info = take((MOE_MAX_IDS + 1) * moe::kSlotInfoBytes);
+  L->slot_info = take((size_t)(MOE_MAX_IDS + 1) * moe::kSlotInfoBytes);
   L->segments = take(sizeof(int32_t) + (size_t)moe::kMaxDownSegs * (sizeof(int32_t) + sizeof(uint32_t)) +
                      (size_t)(moe::kMaxDownSegs + 1) * sizeof(int32_t));
   L->act = take((size_t)moe::kMaxPairs * imax * sizeof(uint16_t));
@@ -480,7 +498,7 @@ moe_status moe_forward_prefill(const moe_config* cfg, const moe_weights* w, cons
   if (rows < 1) return fail(MOE_ERR_INVALID_ARG, "rows=%d must be positive", rows);
   moe_status st = check_config(cfg);
   if (st) return st;
-  const int chunk = MOE_MAX_IDS / cfg->top_k < MOE_MAX_ROWS ? MOE_MAX_IDS / cfg->top_k : MOE_MAX_ROWS;
+  const int chunk = max_rows(cfg);
   if (!x_bf16 || !out_bf16) return fail(MOE_ERR_INVALID_ARG, "x and out must be device pointers");
   const size_t xb = (size_t)rows * cfg->hidden * sizeof(uint16_t);
   if (overlaps(x_bf16, xb, out_bf16, xb)) return fail(MOE_ERR_INVALID_ARG, "x and out overlap");

@@ -12,10 +12,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kChunk = 2048;        // K columns one wave covers per pass: 64 lanes x 32 columns
 constexpr int kChunkUnits = 256;    // 16-byte bf16 units per chunk (2048 * 2 B / 16 B)
-constexpr int kMaxRows = 8;
-constexpr int kMaxIds = 64;
-constexpr int kSharedSlot = 64;     // slot table index of the shared expert
-constexpr int kNumSlots = 65;
+constexpr int kMaxRows = 16;
+constexpr int kMaxIds = 128;
+constexpr int kSharedSlot = 128;    // slot table index of the shared expert
+constexpr int kNumSlots = 129;
 
 // Weight pointers of one union slot (a routed expert, or the shared expert at
 // kSharedSlot), resolved once per call so the sweeps need a single load.

@@ -32,9 +32,9 @@ struct RouteParams {
   const float* bias;       // [E]; for softmax any readable [E] floats (ignored)
   int E, k, rows, route_kind, norm;
   float rsf;
-  float* logits;           // [8][E]
-  double* score;           // [8][E] sigmoid(logit) in fp64 (sigmoid routing)
-  float* gamma;            // [8]
+  float* logits;           // [MOE_MAX_ROWS][E]
+  double* score;           // [MOE_MAX_ROWS][E] sigmoid(logit) in fp64 (sigmoid routing)
+  float* gamma;            // [MOE_MAX_ROWS]
   int32_t* ids_out;        // [rows][k]
   float* w_out;            // [rows][k]
   // union outputs (moe_forward only)
@@ -42,7 +42,7 @@ struct RouteParams {
   int32_t* union_count;
   int32_t* slot_to_union;
   uint32_t* row_mask;
-  SlotInfo* slots;         // [65]
+  SlotInfo* slots;         // [MOE_MAX_IDS + 1]
   int expert_lo, expert_hi; // experts swept: the union keeps ids in [lo, hi) (all of [0, E) but under EP)
   int ungated;             // 1: no shared-expert gate vector, gamma = 1 (gate_vec then points at any h floats)
   moe_expert_table gate, up, down;
@@ -52,7 +52,7 @@ struct RouteParams {
 
 struct SweepParams {
   const uint16_t* x;          // [rows][h] bf16
-  const SlotInfo* slots;      // [65] (down sweep; written by the gate/up sweep)
+  const SlotInfo* slots;      // [MOE_MAX_IDS + 1] (down sweep; written by the gate/up sweep)
   const int32_t* union_count; // device U (down sweep)
   uint16_t* act;              // [pairs][act_stride] bf16, by (row, expert) pair
   float* y;                   // [pairs][h] fp32, by (row, expert) pair
@@ -70,7 +70,7 @@ struct SweepParams {
   float* partial;             // [rows][h] fp32 routed partial (expert-parallel share), or null
 };
 
-constexpr size_t kSlotInfoBytes = 80;  // sizeof(SlotInfo), checked in the kernels file
+constexpr size_t kSlotInfoBytes = 88;  // sizeof(SlotInfo), checked in the kernels file
 
 // Optional kernel start/stop events (hipExtLaunchKernel): the events record
 // the kernel's own start and end, with nothing enqueued between kernels.

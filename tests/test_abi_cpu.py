@@ -76,10 +76,10 @@ def test_workspace_layout_is_ordered_and_aligned():
     assert offs == sorted(offs) and len(set(offs)) == len(offs)
     assert all(o % 256 == 0 for o in offs)
     assert L.total == moe.moe_workspace_bytes(cfg)
-    # act holds 64 + 8 (row, expert) pairs x max(I, Is) bf16; y 72 pairs x h fp32
-    assert L.y - L.act >= 72 * 2048 * 2
-    assert L.total - L.y >= 72 * 6144 * 4
-    assert L.total < 4 << 20
+    # act holds 128 + 16 (row, expert) pairs x max(I, Is) bf16; y 144 pairs x h fp32
+    assert L.y - L.act >= 144 * 2048 * 2
+    assert L.total - L.y >= 144 * 6144 * 4
+    assert L.total < 5 << 20
     assert lib.moe_workspace_bytes(ctypes.byref(cfg_c4(hidden=100))) == 0
 
 
@@ -94,15 +94,23 @@ def test_bad_config_refused(field, value):
     assert lib.moe_last_error().decode()
 
 
-@pytest.mark.parametrize("rows", [0, 9, -1])
+@pytest.mark.parametrize("rows", [0, 17, -1])
 def test_bad_rows_refused(rows):
     assert forward(cfg_c4(), fake_weights(), rows=rows) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_too_many_ids_refused():
-    # top_k * rows > 64: more ids than one block deduplicates
-    assert forward(cfg_c4(top_k=16), fake_weights(), rows=5) == moe.MOE_ERR_INVALID_ARG
-    assert "64" in lib.moe_last_error().decode()
+    # top_k * rows > 128: more ids than the union's two 64-slot tiles
+    assert forward(cfg_c4(top_k=16), fake_weights(), rows=9) == moe.MOE_ERR_INVALID_ARG
+    assert "128" in lib.moe_last_error().decode()
+
+
+def test_rows_beyond_staged_x_refused():
+    # rows * ceil(hidden / 2048) > 36: x for every row does not fit the gate/up
+    # sweep's LDS; 12 rows fit at hidden 6144 (3 chunks), 16 at hidden 4096
+    assert forward(cfg_c4(), fake_weights(), rows=13) == moe.MOE_ERR_UNSUPPORTED
+    assert "moe_forward_prefill" in lib.moe_last_error().decode()
+    assert forward(cfg_c4(hidden=8192), fake_weights(), rows=10) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_pointer_refusals():
@@ -146,8 +154,8 @@ def test_union_refusals():
     u = lambda rows, k, E, ids=X, uid=OUT, cnt=OUT + 512, s2u=OUT + 1024, rm=OUT + 2048: lib.moe_union(
         ids, rows, k, E, uid, cnt, s2u, rm, None)
     assert u(0, 8, 256) == moe.MOE_ERR_INVALID_ARG
-    assert u(9, 1, 256) == moe.MOE_ERR_INVALID_ARG
-    assert u(8, 9, 256) == moe.MOE_ERR_INVALID_ARG      # 72 ids
+    assert u(17, 1, 256) == moe.MOE_ERR_INVALID_ARG
+    assert u(16, 9, 256) == moe.MOE_ERR_INVALID_ARG     # 144 ids
     assert u(2, 8, 4) == moe.MOE_ERR_INVALID_ARG        # top_k > num_experts
     assert u(1, 8, 256, ids=0) == moe.MOE_ERR_INVALID_ARG
     assert u(1, 8, 256, s2u=OUT + 64) == moe.MOE_ERR_INVALID_ARG  # overlaps union_ids
@@ -160,7 +168,7 @@ def test_route_refusals():
                                                wts, WS, need, None)
     assert r(0, OUT) == moe.MOE_ERR_INVALID_ARG
     assert r(OUT, OUT + 16) == moe.MOE_ERR_INVALID_ARG   # ids and weights overlap
-    assert r(OUT, OUT + 4096, rows=9) == moe.MOE_ERR_INVALID_ARG
+    assert r(OUT, OUT + 4096, rows=17) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_stage_names():
@@ -184,8 +192,8 @@ def test_token_major_refuses_like_forward():
 
     cases = [
         (cfg_c4(hidden=100), fake_weights(), {}),
-        (cfg_c4(), fake_weights(), {"rows": 9}),
-        (cfg_c4(top_k=16), fake_weights(), {"rows": 5}),
+        (cfg_c4(), fake_weights(), {"rows": 17}),
+        (cfg_c4(top_k=16), fake_weights(), {"rows": 9}),
         (cfg_c4(), None, {}),
         (cfg_c4(), fake_weights(), {"out": X + 64}),
         (cfg_c4(), fake_weights(sigmoid=False), {}),
@@ -212,7 +220,7 @@ def test_ep_refusals():
     assert ep(0, 32, partial=P + 4) == moe.MOE_ERR_INVALID_ARG         # misaligned
     assert ep(0, 32, partial=X + 256) == moe.MOE_ERR_INVALID_ARG       # overlaps x
     assert ep(0, 32, partial=WS + 4096) == moe.MOE_ERR_INVALID_ARG     # inside the workspace
-    assert ep(0, 32, rows=9) == moe.MOE_ERR_INVALID_ARG
+    assert ep(0, 32, rows=17) == moe.MOE_ERR_INVALID_ARG
 
     def comb(red, out, rows=4, ws_bytes=need):
         return lib.moe_ep_combine(ctypes.byref(cfg), red, out, rows, WS, ws_bytes, None)
@@ -225,7 +233,7 @@ def test_ep_refusals():
     u = lambda lo, hi, E=256: lib.moe_union_local(X, 2, 8, E, lo, hi, OUT, OUT + 512, OUT + 1024, OUT + 2048, None)
     for lo, hi in [(-1, 4), (5, 4), (0, 300)]:
         assert u(lo, hi) == moe.MOE_ERR_INVALID_ARG, (lo, hi)
-    assert lib.moe_union_local(X, 9, 8, 256, 0, 8, OUT, OUT + 512, OUT + 1024, OUT + 2048, None) == \
+    assert lib.moe_union_local(X, 17, 8, 256, 0, 8, OUT, OUT + 512, OUT + 1024, OUT + 2048, None) == \
         moe.MOE_ERR_INVALID_ARG
 
 
@@ -273,7 +281,7 @@ def test_static_forward_refusals():
     st = lambda rows=4, x=X, out=OUT, w=None, c=cfg: lib.moe_forward_static(
         ctypes.byref(c), ctypes.byref(w or fake_weights()), x, out, rows, None)
     assert st(rows=0) == moe.MOE_ERR_INVALID_ARG
-    assert st(rows=9) == moe.MOE_ERR_INVALID_ARG
+    assert st(rows=17) == moe.MOE_ERR_INVALID_ARG
     assert st(x=0) == moe.MOE_ERR_INVALID_ARG
     assert st(out=0) == moe.MOE_ERR_INVALID_ARG
     assert st(x=X + 2) == moe.MOE_ERR_INVALID_ARG                # misaligned

@@ -40,14 +40,15 @@ def read_intermediates(dl, ws, rows):
     imax = max(dl.cfg.moe_inter, dl.cfg.shared_inter)
     P = rows * (k + 1)
     U = int(ws_read(ws, L.union_count, np.int32, 1)[0])
+    M, N = moe.MOE_MAX_ROWS, moe.MOE_MAX_IDS
     return dict(
-        ids=ws_read(ws, L.topk_ids, np.int32, 8 * k).reshape(8, k)[:rows],
-        weights=ws_read(ws, L.topk_w, np.float32, 8 * k).reshape(8, k)[:rows],
-        gamma=ws_read(ws, L.gamma, np.float32, 8)[:rows],
+        ids=ws_read(ws, L.topk_ids, np.int32, M * k).reshape(M, k)[:rows],
+        weights=ws_read(ws, L.topk_w, np.float32, M * k).reshape(M, k)[:rows],
+        gamma=ws_read(ws, L.gamma, np.float32, M)[:rows],
         union_count=U,
-        union_ids=ws_read(ws, L.union_ids, np.int32, 64)[:U],
+        union_ids=ws_read(ws, L.union_ids, np.int32, N)[:U],
         slot_to_union=ws_read(ws, L.slot_to_union, np.int32, rows * k),
-        row_mask=ws_read(ws, L.row_mask, np.uint32, 64)[:U],
+        row_mask=ws_read(ws, L.row_mask, np.uint32, N)[:U],
         act=ws_read(ws, L.act, np.uint16, P * imax).reshape(P, imax),
         y=ws_read(ws, L.y, np.float32, P * h).reshape(P, h),
     )
@@ -341,15 +342,15 @@ def test_union_local_matches_oracle():
     for _ in range(60):
         E = int(rng.integers(4, 300))
         k = int(rng.integers(1, min(E, 8) + 1))
-        R = min(8, int(rng.integers(1, 64 // k + 1)))
+        R = min(16, int(rng.integers(1, 128 // k + 1)))
         ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(R)]).astype(np.int32)
         lo = int(rng.integers(0, E + 1))
         hi = int(rng.integers(lo, E + 1))
         d_ids = torch.from_numpy(ids).cuda()
-        uid = torch.full((64,), -7, dtype=torch.int32, device="cuda")
+        uid = torch.full((moe.MOE_MAX_IDS,), -7, dtype=torch.int32, device="cuda")
         cnt = torch.full((1,), -7, dtype=torch.int32, device="cuda")
         s2u = torch.full((R * k,), -7, dtype=torch.int32, device="cuda")
-        msk = torch.zeros(64, dtype=torch.int32, device="cuda")
+        msk = torch.zeros(moe.MOE_MAX_IDS, dtype=torch.int32, device="cuda")
         moe.moe_union_local(d_ids, lo, hi, uid, cnt, s2u, msk, num_experts=E)
         torch.cuda.synchronize()
         u, U, ls2u, lmask = expert_union_local(ids, lo, hi)
@@ -476,6 +477,49 @@ def test_forward_nvfp4_router(name):
     check_token_major(dl, x)
 
 
+# ---------------------------------------------------------------- more than 8 rows: the two-tile union
+# Up to 16 rows and 128 ids in one call: the union of all rows' experts over
+# two 64-slot tiles, each union expert swept once for every row that chose it
+# (the "amortize PARTIALLY" note's union, past the "WIDENED (2026-08-31)"
+# note's 64-id block).
+def test_forward_16_rows_two_tile_union():
+    shape = dataclasses.replace(synth.CONFIGS["c2_e128_verify2"], rows=16, name="c2_rows16")
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = synth.activations(shape, 2, rows=16)
+    got, _, _ = check_against_oracle(weights, dl, x, rows_checked=[0, 5, 9, 15])
+    singles = np.stack([run_forward(dl, x[r:r + 1])[0][0] for r in range(16)])
+    assert np.array_equal(got, singles)
+    for R in (9, 12, 13):
+        sub, _ = run_forward(dl, x[:R])
+        assert np.array_equal(sub, singles[:R]), R
+    check_token_major(dl, x)
+    check_ep_shares(weights, dl, x, [(0, 40), (40, 128)], rows_checked=[3, 12])
+
+
+def test_forward_12_rows_256_experts(layer256):
+    # 12 rows at hidden 6144 (36 staged chunks of x, the most one call takes)
+    weights, dl = layer256
+    shape = dataclasses.replace(synth.CONFIGS["c3_e256_verify4"], rows=12, name="c3_rows12")
+    w12 = dataclasses.replace(weights, shape=shape)
+    x = synth.activations(shape, 1, rows=12)
+    got, ref, _ = check_against_oracle(w12, dl, x, rows_checked=[0, 4, 8, 11])
+    assert ref["union_count"] > 0
+    singles = np.stack([run_forward(dl, x[r:r + 1])[0][0] for r in range(12)])
+    assert np.array_equal(got, singles)
+    check_token_major(dl, x)
+
+
+def test_forward_16_rows_k8_more_experts():
+    # 128 ids, E > 256 (16 top-k keys per lane), rows beyond one tile
+    shape = synth.MoeShape("e512_rows16", 1024, 512, 8, 64, 96, 16, synth.ROUTE_SIGMOID_BIAS, True, 2.5)
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = synth.activations(shape, 0)
+    check_against_oracle(weights, dl, x)
+    check_token_major(dl, x)
+
+
 # ---------------------------------------------------------------- more than 256 experts
 # Past 256 experts the gate/up sweep keeps 16 top-k keys per lane and reads
 # each union slot's weight pointers from the expert tables instead of an LDS
@@ -586,10 +630,10 @@ def test_no_write_outside_buffers(name):
     part_all, part_u8 = guarded(torch, R * h * 4)
     ids_all, ids_u8 = guarded(torch, R * k * 4)
     w_all, w_u8 = guarded(torch, R * k * 4)
-    uid_all, uid_u8 = guarded(torch, 64 * 4)
+    uid_all, uid_u8 = guarded(torch, moe.MOE_MAX_IDS * 4)
     cnt_all, cnt_u8 = guarded(torch, 4)
     s2u_all, s2u_u8 = guarded(torch, R * k * 4)
-    msk_all, msk_u8 = guarded(torch, 64 * 4)
+    msk_all, msk_u8 = guarded(torch, moe.MOE_MAX_IDS * 4)
     out = out_u8.view(torch.int16).view(R, h)
     part = part_u8.view(torch.float32).view(R, h)
     ids = ids_u8.view(torch.int32).view(R, k)
@@ -604,7 +648,8 @@ def test_no_write_outside_buffers(name):
                         s2u_u8.view(torch.int32), msk_u8.view(torch.int32), num_experts=shape.num_experts)
     torch.cuda.synchronize()
     for whole, n in ((ws_all, wsn), (out_all, R * h * 2), (part_all, R * h * 4), (ids_all, R * k * 4),
-                     (w_all, R * k * 4), (uid_all, 256), (cnt_all, 4), (s2u_all, R * k * 4), (msk_all, 256)):
+                     (w_all, R * k * 4), (uid_all, moe.MOE_MAX_IDS * 4), (cnt_all, 4), (s2u_all, R * k * 4),
+                     (msk_all, moe.MOE_MAX_IDS * 4)):
         assert guards_intact(whole, n)
 
 
@@ -622,7 +667,7 @@ def test_graph_capture_every_call():
     ws_a, ws_b = ws_for(dl.cfg), ws_for(dl.cfg)
     ids = torch.zeros((R, k), dtype=torch.int32, device="cuda")
     wts = torch.zeros((R, k), dtype=torch.float32, device="cuda")
-    uid = torch.zeros(64, dtype=torch.int32, device="cuda")
+    uid = torch.zeros(moe.MOE_MAX_IDS, dtype=torch.int32, device="cuda")
     cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
     s2u = torch.zeros(R * k, dtype=torch.int32, device="cuda")
     tm = torch.zeros((R, h), dtype=torch.int16, device="cuda")
@@ -670,7 +715,10 @@ def test_graph_capture_every_call():
 
 # ---------------------------------------------------------------- more rows than one block: prefill sub-chunks
 PREFILL = [
+    # 20 rows at hidden 4096: sub-chunks of 16 and 4 rows
     (dataclasses.replace(synth.CONFIGS["c2_e128_verify2"], rows=20, name="c2_rows20"), [0, 9, 19]),
+    # 30 rows at hidden 6144: sub-chunks of 12, 12 and 6 rows
+    (synth.MoeShape("h6144_rows30", 6144, 32, 8, 64, 64, 30, synth.ROUTE_SIGMOID_BIAS, True, 2.5), [0, 13, 29]),
     (synth.MoeShape("k16_rows11", 512, 32, 16, 64, 96, 11, synth.ROUTE_SIGMOID_BIAS, True, 2.5), None),
 ]
 

@@ -166,10 +166,10 @@ def run_union(ids_np, E):
     torch = torch_cuda()
     moe = moe_mod()
     ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).cuda()
-    uid = torch.full((64,), -7, dtype=torch.int32, device="cuda")
+    uid = torch.full((moe.MOE_MAX_IDS,), -7, dtype=torch.int32, device="cuda")
     cnt = torch.full((1,), -7, dtype=torch.int32, device="cuda")
     s2u = torch.full((ids_np.size,), -7, dtype=torch.int32, device="cuda")
-    rmask = torch.zeros((64,), dtype=torch.int32, device="cuda")
+    rmask = torch.zeros((moe.MOE_MAX_IDS,), dtype=torch.int32, device="cuda")
     moe.moe_union(ids, uid, cnt, s2u, rmask, num_experts=E)
     torch.cuda.synchronize()
     U = int(cnt.item())
@@ -197,12 +197,34 @@ def test_union_random():
         check_union(ids, E)
 
 
+def test_union_random_two_tiles():
+    # More than 64 ids (rows up to 16, top_k * rows up to 128): the scan runs
+    # over two 64-slot tiles; first occurrences in the second tile continue the
+    # union positions of the first, and a slot in the second tile may repeat
+    # an id first seen in the first.
+    rng = np.random.default_rng(8)
+    for trial in range(200):
+        E = int(rng.integers(16, 1025))
+        k = int(rng.integers(1, 17))
+        R = int(rng.integers(1, min(16, 128 // k) + 1))
+        pool = min(E, int(rng.integers(k, 4 * k + 1)))
+        ids = np.stack([rng.choice(pool, size=k, replace=False) for _ in range(R)]).astype(np.int32)
+        check_union(ids, E)
+
+
 def test_union_extremes():
     check_union(np.tile(np.arange(8, dtype=np.int32), (8, 1)), 256)        # U = k
     check_union(np.arange(64, dtype=np.int32).reshape(8, 8)[:, ::-1], 256)  # U = 64
     check_union(np.array([[255, 0, 128, 7]], np.int32), 256)              # one row
     check_union(np.array([[5], [5], [5]], np.int32), 16)                  # k = 1
     check_union(np.arange(64, dtype=np.int32)[::-1].reshape(1, 64), 64)   # k = 64, one row
+    check_union(np.arange(128, dtype=np.int32).reshape(16, 8), 256)       # U = 128
+    check_union(np.tile(np.arange(8, dtype=np.int32), (16, 1)), 256)       # 128 ids, U = 8
+    check_union(np.arange(128, dtype=np.int32)[::-1].reshape(2, 64), 128)  # k = 64, two rows
+    # the second tile's first slot repeats the first tile's last id
+    ids = np.arange(72, dtype=np.int32).reshape(9, 8)
+    ids[8, 0] = 63
+    check_union(ids, 256)
 
 
 # ---------------------------------------------------------------- NVFP4 router

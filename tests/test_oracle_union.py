@@ -67,6 +67,22 @@ def test_union_random_large():
         _check(ids)
 
 
+def test_union_past_64_ids():
+    # 65..128 ids (up to 16 rows): the definition does not change with the
+    # number of ids; checked against dict.fromkeys with ids repeated across the
+    # 64th slot
+    rng = np.random.default_rng(22)
+    for _ in range(300):
+        k = int(rng.integers(1, 17))
+        R = int(rng.integers(max(1, 65 // k), 128 // k + 1)) if 128 // k >= 1 else 1
+        R = max(1, min(R, 16))
+        pool = int(rng.integers(k, 4 * k + 1))
+        ids = np.stack([rng.choice(pool, size=k, replace=False) for _ in range(R)])
+        _check(ids)
+    _check(np.arange(128).reshape(16, 8))
+    _check(np.tile(np.arange(8), (16, 1)))
+
+
 # ---------------------------------------------------------------- one rank's share (expert parallel)
 from oracle.union import expert_union_local  # noqa: E402
 
