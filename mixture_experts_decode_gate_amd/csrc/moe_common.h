@@ -428,23 +428,30 @@ __device__ __forceinline__ SlotInfo shared_slot_info(const RouteParams& rp, uint
   return si;
 }
 
-// Down-sweep segments (one wave): a segment is one union slot and a group of
-// up to kDownGroup of the rows that use it, routed slots in union order, then
-// the shared slot's groups of all R rows.  Lane l holds the row masks of
-// slots l (mask0) and 64 + l (mask1), 0 past U.  seg_rows[s] holds row i of
-// the group in bits 4i..4i+3 and the row count in bits 28..31; seg_cum[s] is
-// the summed work weight of the segments before s (seg_cum[count] the total).
-// Returns the number of segments.
+// Down-sweep segments (one wave): one segment per slot -- the shared slot
+// first (all R rows), then the routed slots in union order.  Lane l holds the
+// row masks of union slots l (mask0) and 64 + l (mask1), 0 past U.
+// seg_rows[s] holds the segment's row mask in bits 0..15 and its number of
+// row groups (of up to kDownGroup rows) in bits 16..23; seg_cum[s] is the
+// summed work weight of the segments before s (kSegCostBase per group plus
+// one per row; seg_cum[count] the total).  Returns the number of segments.
 inline __device__ int build_segments(uint32_t mask0, uint32_t mask1, int lane, int R, int32_t* seg_slot,
-                              uint32_t* seg_rows, int32_t* seg_cum) {
-  int total = 0, wtotal = 0;  // segments and weight of the slots before this tile
+                                     uint32_t* seg_rows, int32_t* seg_cum) {
+  const int sh_groups = (R + kDownGroup - 1) / kDownGroup;
+  if (lane == 0) {
+    seg_slot[0] = kSharedSlot;
+    seg_rows[0] = ((1u << R) - 1u) | ((uint32_t)sh_groups << 16);
+    seg_cum[0] = 0;
+  }
+  int total = 1, wtotal = kSegCostBase * sh_groups + R;  // segments and weight so far
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const uint32_t mask = q ? mask1 : mask0;
     const int cnt = __popc(mask);
     const int groups = (cnt + kDownGroup - 1) / kDownGroup;
-    int incl = groups;                        // inclusive prefix sums over lanes: segments
-    int wincl = groups * kSegCostBase + cnt;  // and weight
+    const int has = cnt > 0 ? 1 : 0;
+    const int cost = kSegCostBase * groups + cnt;
+    int incl = has, wincl = cost;  // inclusive prefix sums over lanes
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(incl, o), wv = __shfl_up(wincl, o);
@@ -453,37 +460,14 @@ inline __device__ int build_segments(uint32_t mask0, uint32_t mask1, int lane, i
         wincl += wv;
       }
     }
-    const int seg = total + incl - groups;
-    int wcum = wtotal + wincl - (groups * kSegCostBase + cnt);
-    for (int g = 0; g < groups; ++g) {
-      uint32_t packed = 0;
-      int n = 0;
-      for (int r = 0; r < kMaxRows && n < kDownGroup; ++r) {
-        // rows of earlier groups are skipped
-        if (((mask >> r) & 1u) && __popc(mask & ((1u << r) - 1u)) >= g * kDownGroup) {
-          packed |= (uint32_t)r << (4 * n);
-          ++n;
-        }
-      }
-      seg_slot[seg + g] = 64 * q + lane;
-      seg_rows[seg + g] = packed | ((uint32_t)n << 28);
-      seg_cum[seg + g] = wcum;
-      wcum += kSegCostBase + n;
+    if (has) {
+      const int seg = total + incl - 1;
+      seg_slot[seg] = 64 * q + lane;
+      seg_rows[seg] = mask | ((uint32_t)groups << 16);
+      seg_cum[seg] = wtotal + wincl - cost;
     }
     total += __shfl(incl, 63);
     wtotal += __shfl(wincl, 63);
-  }
-  for (int g = 0; g * kDownGroup < R; ++g) {
-    uint32_t packed = 0;
-    int n = 0;
-    for (int r = g * kDownGroup; r < R && n < kDownGroup; ++r, ++n) packed |= (uint32_t)r << (4 * n);
-    if (lane == 0) {
-      seg_slot[total] = kSharedSlot;
-      seg_rows[total] = packed | ((uint32_t)n << 28);
-      seg_cum[total] = wtotal;
-    }
-    wtotal += kSegCostBase + n;
-    ++total;
   }
   if (lane == 0) seg_cum[total] = wtotal;
   return total;
@@ -500,6 +484,7 @@ constexpr int kMaxDevices = 64;
 // loads in flight per lane (the fastest of 4 / 8 / 16 each).
 constexpr int kGateupWavesPerCU = 8;
 constexpr int kDownWavesPerCU = 12;
+constexpr int kNumXcds = 8;  // accelerator dies; workgroups go to them round-robin
 constexpr int kProbeBlocksPerCU = 16;
 constexpr int kProbeUnroll = 16;
 

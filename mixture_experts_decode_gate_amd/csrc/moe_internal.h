@@ -14,10 +14,10 @@ struct SlotInfo;
 // pair t = r * k + j for row r's j-th routed expert, rows * k + r for row r's
 // shared expert.
 constexpr int kMaxPairs = MOE_MAX_IDS + MOE_MAX_ROWS;
-constexpr int kDownGroup = 2;  // act rows a down segment carries
-constexpr int kMaxDownSegs = (MOE_MAX_IDS + 1) * ((MOE_MAX_ROWS + kDownGroup - 1) / kDownGroup);
-// Down-sweep work weight of a segment with n rows: kSegCostBase + n per
-// weight row (decode and loads, plus one dot product per row).
+constexpr int kDownGroup = 2;  // act rows a down-sweep wave holds
+constexpr int kMaxDownSegs = MOE_MAX_IDS + 1;  // one segment per union slot and the shared slot
+// Down-sweep work weight of a group of n rows: kSegCostBase + n per weight
+// row (decode and loads, plus one dot product per row).
 constexpr int kSegCostBase = 3;
 
 struct RouteParams {

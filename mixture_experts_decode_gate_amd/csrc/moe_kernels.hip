@@ -206,10 +206,10 @@ template <int NCH>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   constexpr int kGroup = kDownGroup;  // act rows held per segment (16 VGPRs each per 2048 columns)
   constexpr int kMaxSegs = kMaxDownSegs;
-  static_assert(kMaxSegs < 2048, "the segment search spans at most 2047 segments");
+  static_assert(kMaxSegs < 256, "the segment search spans at most 255 segments");
   __shared__ SlotInfo s_slots[kNumSlots];
   __shared__ int s_seg_slot[kMaxSegs];
-  __shared__ uint32_t s_seg_rows[kMaxSegs];  // row i of the group in bits 4i..4i+3, count in bits 28..31
+  __shared__ uint32_t s_seg_rows[kMaxSegs];  // row mask in bits 0..15, row groups in bits 16..23
   __shared__ int s_seg_cum[kMaxSegs + 1];    // work weight before segment s
   __shared__ int s_nseg;
   const int lane = threadIdx.x & 63;
@@ -245,25 +245,36 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   }
   __syncthreads();
 
-  // Each segment gets a group of waves in proportion to its work weight
-  // (kSegCostBase + rows per weight row: a two-row segment costs more
-  // arithmetic per byte): with cumulative weights c_s and total C, virtual
-  // wave v of V works on the segment s with c_s <= v * C / V < c_{s+1}.  The
-  // group's waves take interleaved batches of kDownBatch rows: every group
-  // sweeps its matrix front to back together.  V >= C gives every segment
-  // at least one virtual wave; with fewer waves than that a wave takes
-  // several virtual waves in turn.
+  // Each segment (a slot) gets waves in proportion to its work weight
+  // (kSegCostBase + rows per weight row and group of rows: a two-row group
+  // costs more arithmetic per byte): with cumulative weights c_s and total C,
+  // virtual wave v of V works on the segment s with c_s <= v * C / V <
+  // c_{s+1}.  Within a segment of G row groups, consecutive virtual waves take
+  // groups 0, 1, .., G-1 of the same batch: the waves that read a weight row
+  // for the slot's different row groups sit side by side (the shared slot,
+  // first, starts at wave 0, so at 8 rows its four groups share each block)
+  // and the repeated reads are served by the cache.  Each group's waves take
+  // interleaved batches of kDownBatch rows: every group sweeps its matrix
+  // front to back together.  V >= C gives every segment at least 4 G virtual
+  // waves (a segment weighs at least 4 per group); with fewer waves than that
+  // a wave takes several virtual waves in turn.
   const int W = gridDim.x * nwaves;
   const int nseg = s_nseg;
   const int C = s_seg_cum[nseg];
   const int V = W > C ? W : C;
 
+  // Workgroup b runs on XCD b % 8; numbering the blocks XCD by XCD gives each
+  // XCD (and its L2) a contiguous run of virtual waves, so the row groups of
+  // one slot and the readers of one act row mostly share an L2.
+  const int nb = (int)gridDim.x, b = (int)blockIdx.x;
+  const int lb = nb % kNumXcds == 0 ? (b % kNumXcds) * (nb / kNumXcds) + b / kNumXcds : b;
+
   DownBatch<NCH> buf[kDownBufs];
   u32x4 act[kGroup][NCH][4];
-  for (int v = blockIdx.x * nwaves + wave; v < V; v += W) {
+  for (int v = lb * nwaves + wave; v < V; v += W) {
     const long long key = (long long)v * C / V;  // in [0, C)
     int seg = 0;
-    for (int span = 1024; span > 0; span >>= 1)  // largest s with c_s <= key (nseg <= kMaxSegs)
+    for (int span = 128; span > 0; span >>= 1)  // largest s with c_s <= key (nseg <= kMaxSegs)
       if (seg + span < nseg && s_seg_cum[seg + span] <= key) seg += span;
     seg = uniform_int(seg);
     const long long c0 = s_seg_cum[seg], c1 = s_seg_cum[seg + 1];
@@ -271,23 +282,40 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
     const int last = (int)(((long long)V * c1 + C - 1) / C);
     const int n_end = h;
     const int slot = uniform_int(s_seg_slot[seg]);
-    const uint32_t rows = uniform_u32(s_seg_rows[seg]);
-    const int cnt = (int)(rows >> 28);
+    const uint32_t segw = uniform_u32(s_seg_rows[seg]);
+    const uint32_t mask = segw & 0xFFFFu;
+    const int ngroups = (int)(segw >> 16);
+    const int vi = v - first, nvs = last - first;
+    // Every row group gets the same number of waves, so that the i-th waves
+    // of all groups read the same batches; the at most ngroups - 1 virtual
+    // waves left over stay idle.
+    const int wg = nvs / ngroups;  // >= 1: the segment weighs at least 4 per group
+    if (vi >= wg * ngroups) continue;
+    const int grp = vi % ngroups;  // this wave's row group
     const SlotInfo& si = s_slots[slot];
     const int K = uniform_int(si.inter);
     const uint8_t* const d_packed = uniform_ptr(si.down_packed);
     const uint8_t* const d_scales = uniform_ptr(si.down_scales);
     const float d2 = uniform_f32(si.down_scale2);
-    const int stride = (last - first) * kDownBatch;
-    const int n0 = (v - first) * kDownBatch;
+    const int stride = wg * kDownBatch;
+    const int n0 = (vi / ngroups) * kDownBatch;
     if (n0 >= n_end) continue;
-    // Pair index of each group row (unused entries repeat the last row).
+    // The group's rows: the (kGroup * grp)-th and following rows of the mask;
+    // their pair indices (unused entries repeat the last row).
+    int grow[kGroup], cnt = 0;
+    for (int r = 0; r < kMaxRows; ++r) {
+      if ((mask >> r) & 1u) {
+        const int idx = __popc(mask & ((1u << r) - 1u)) - kGroup * grp;
+        if (idx >= 0 && idx < kGroup) {
+          grow[idx] = r;
+          ++cnt;
+        }
+      }
+    }
+    cnt = uniform_int(cnt);
     int prs[kGroup];
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      const int r = (int)((rows >> (4 * (i < cnt ? i : cnt - 1))) & 0xFu);
-      prs[i] = uniform_int(si.pair[r]);
-    }
+    for (int i = 0; i < kGroup; ++i) prs[i] = uniform_int(si.pair[grow[i < cnt ? i : cnt - 1]]);
     // act rows of the group.  Lanes past K read the row's first columns:
     // finite values that meet zeroed scales.
 #pragma unroll
@@ -428,7 +456,46 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
   // slot table, U, routing weights and gates, then a shared-expert unit's
   // weights (their pointers are this kernel's arguments); (2) once the slot
   // table is in LDS, the first routed unit's weights; (3) the act rows, staged
-  // while those weights are in flight.  Loads are consumed in issue order.
+  // while those weights are in flight.  With one or two rows the act rows are
+  // few and go out with step (1) instead, saving a round trip.  Loads are
+  // consumed in issue order.
+  constexpr bool kActFirst = R <= 2;
+  const int units = P * NCH * kChunkUnits;
+  // Unit i of the act staging is 16 bytes of pair t, chunk c, unit un
+  // (columns past the pair's K read a valid copy and are stored as zeros).
+  auto act_src = [&](int i, int& dst, bool& valid) {
+    const int t = i / (NCH * kChunkUnits);
+    const int rem = i - t * NCH * kChunkUnits;
+    const int c = rem / kChunkUnits, un = rem - c * kChunkUnits;
+    const int K = t < R * k ? p.inter : p.shared_inter;
+    const int col = c * kChunk + un * 8;
+    valid = col < K;
+    dst = (t * NCH + c) * kChunkUnits + swz_unit(un);
+    return reinterpret_cast<const u32x4*>(p.act + (size_t)t * p.act_stride + (valid ? col : 0));
+  };
+  auto act_issue = [&](u32x4* av, int base, int n) {
+#pragma unroll
+    for (int q = 0; q < n; ++q) {
+      const int i = base + (int)threadIdx.x + q * kDbThreads;
+      int dst;
+      bool valid;
+      av[q] = ld_global(act_src(i < units ? i : 0, dst, valid));
+    }
+  };
+  auto act_store = [&](const u32x4* av, int base, int n) {
+#pragma unroll
+    for (int q = 0; q < n; ++q) {
+      const int i = base + (int)threadIdx.x + q * kDbThreads;
+      if (i < units) {
+        int dst;
+        bool valid;
+        act_src(i, dst, valid);
+        s_act[dst] = valid ? av[q] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < n; ++q) asm volatile("" ::"v"(av[q]));
+  };
   constexpr int kSlotWords = (int)(sizeof(SlotInfo) / 4);
   constexpr int kTabPer = (kNumSlots * kSlotWords + kDbThreads - 1) / kDbThreads;
   uint32_t tab[kTabPer];
@@ -442,6 +509,8 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
   const float wv = ld_global(rp.w_out + tw);
   const int s2u = ld_global(rp.slot_to_union + tw);
   const float gv = ld_global(rp.gamma + ((int)threadIdx.x < R ? (int)threadIdx.x : 0));
+  u32x4 av_first[kActFirst ? kDbActPer : 1];
+  if (kActFirst) act_issue(av_first, 0, kDbActPer);
   if (threadIdx.x == 0) {
     s_next = 0;
     s_slots[kSharedSlot] = shared_slot_info(rp, (1u << R) - 1u);
@@ -508,6 +577,7 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
     if ((int)threadIdx.x < R) s_gamma[threadIdx.x] = gv;
 #pragma unroll
     for (int q = 0; q < kTabPer; ++q) asm volatile("" ::"v"(tab[q]));
+    if (kActFirst) act_store(av_first, 0, kDbActPer);
   }
   __syncthreads();
   const int total = (s_union + 1) * nbat;
@@ -525,48 +595,18 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
   }
   fetch(id_b, bb, ib);
 
-  // The act rows: unit i of the staging is 16 bytes of pair t, chunk c,
-  // unit un (columns past the pair's K read a valid copy and are stored as
-  // zeros), in passes of kActPass loads per thread (two at most: the
-  // launcher serves this kernel only when kDbActPer loads per thread cover
-  // every unit).
-  {
-    constexpr int kActPass = R <= 2 ? kDbActPer : kDbActPer / 2;
-    const int units = P * NCH * kChunkUnits;
-    auto act_src = [&](int i, int& dst, bool& valid) {
-      const int t = i / (NCH * kChunkUnits);
-      const int rem = i - t * NCH * kChunkUnits;
-      const int c = rem / kChunkUnits, un = rem - c * kChunkUnits;
-      const int K = t < R * k ? p.inter : p.shared_inter;
-      const int col = c * kChunk + un * 8;
-      valid = col < K;
-      dst = (t * NCH + c) * kChunkUnits + swz_unit(un);
-      return reinterpret_cast<const u32x4*>(p.act + (size_t)t * p.act_stride + (valid ? col : 0));
-    };
+  // Step (3): the act rows, in passes of kActPass loads per thread (two at
+  // most: the launcher serves this kernel only when kDbActPer loads per
+  // thread cover every unit).
+  if (!kActFirst) {
+    constexpr int kActPass = kDbActPer / 2;
     for (int base = 0; base < units; base += kActPass * kDbThreads) {
       u32x4 av[kActPass];
-#pragma unroll
-      for (int q = 0; q < kActPass; ++q) {
-        const int i = base + (int)threadIdx.x + q * kDbThreads;
-        int dst;
-        bool valid;
-        av[q] = ld_global(act_src(i < units ? i : 0, dst, valid));
-      }
-#pragma unroll
-      for (int q = 0; q < kActPass; ++q) {
-        const int i = base + (int)threadIdx.x + q * kDbThreads;
-        if (i < units) {
-          int dst;
-          bool valid;
-          act_src(i, dst, valid);
-          s_act[dst] = valid ? av[q] : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < kActPass; ++q) asm volatile("" ::"v"(av[q]));
+      act_issue(av, base, kActPass);
+      act_store(av, base, kActPass);
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // Rows of a unit in groups of two (act rows from LDS), each weight row
   // decoded once per group; y to LDS and the workspace.
