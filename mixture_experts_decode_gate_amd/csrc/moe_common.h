@@ -432,12 +432,12 @@ __device__ __forceinline__ SlotInfo shared_slot_info(const RouteParams& rp, uint
 // first (all R rows), then the routed slots in union order.  Lane l holds the
 // row masks of union slots l (mask0) and 64 + l (mask1), 0 past U.
 // seg_rows[s] holds the segment's row mask in bits 0..15 and its number of
-// row groups (of up to kDownGroup rows) in bits 16..23; seg_cum[s] is the
+// row groups (of up to ``group`` rows) in bits 16..23; seg_cum[s] is the
 // summed work weight of the segments before s (kSegCostBase per group plus
 // one per row; seg_cum[count] the total).  Returns the number of segments.
-inline __device__ int build_segments(uint32_t mask0, uint32_t mask1, int lane, int R, int32_t* seg_slot,
-                                     uint32_t* seg_rows, int32_t* seg_cum) {
-  const int sh_groups = (R + kDownGroup - 1) / kDownGroup;
+inline __device__ int build_segments(uint32_t mask0, uint32_t mask1, int lane, int R, int group,
+                                     int32_t* seg_slot, uint32_t* seg_rows, int32_t* seg_cum) {
+  const int sh_groups = (R + group - 1) / group;
   if (lane == 0) {
     seg_slot[0] = kSharedSlot;
     seg_rows[0] = ((1u << R) - 1u) | ((uint32_t)sh_groups << 16);
@@ -448,7 +448,7 @@ inline __device__ int build_segments(uint32_t mask0, uint32_t mask1, int lane, i
   for (int q = 0; q < 2; ++q) {
     const uint32_t mask = q ? mask1 : mask0;
     const int cnt = __popc(mask);
-    const int groups = (cnt + kDownGroup - 1) / kDownGroup;
+    const int groups = (cnt + group - 1) / group;
     const int has = cnt > 0 ? 1 : 0;
     const int cost = kSegCostBase * groups + cnt;
     int incl = has, wincl = cost;  // inclusive prefix sums over lanes

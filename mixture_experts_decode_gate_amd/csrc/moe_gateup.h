@@ -307,9 +307,10 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
       *rp.union_count = U;
       rp.slots[kSharedSlot] = s_slots[kSharedSlot];
     }
+    const int kdown = p.inter > p.shared_inter ? p.inter : p.shared_inter;  // the down sweep's K
     const int nseg = build_segments(lane < U ? s_slots[lane].row_mask : 0u,
-                                    64 + lane < U ? s_slots[64 + lane].row_mask : 0u, lane, R, p.seg_slot,
-                                    p.seg_rows, p.seg_cum);
+                                    64 + lane < U ? s_slots[64 + lane].row_mask : 0u, lane, R,
+                                    down_group((kdown + kChunk - 1) / kChunk), p.seg_slot, p.seg_rows, p.seg_cum);
     if (lane == 0) *p.seg_count = nseg;
   }
   if (!has_work) return;

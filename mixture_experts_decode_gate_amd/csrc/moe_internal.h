@@ -14,7 +14,9 @@ struct SlotInfo;
 // pair t = r * k + j for row r's j-th routed expert, rows * k + r for row r's
 // shared expert.
 constexpr int kMaxPairs = MOE_MAX_IDS + MOE_MAX_ROWS;
-constexpr int kDownGroup = 2;  // act rows a down-sweep wave holds
+// act rows a down-sweep wave holds in registers (16 VGPRs per row per 2048
+// columns): four with one 2048-column chunk, two with two
+constexpr int down_group(int nch) { return nch == 1 ? 4 : 2; }
 constexpr int kMaxDownSegs = MOE_MAX_IDS + 1;  // one segment per union slot and the shared slot
 // Down-sweep work weight of a group of n rows: kSegCostBase + n per weight
 // row (decode and loads, plus one dot product per row).

@@ -184,14 +184,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(RouteParams p) {
   topk_select<G>(p, wave, lane, in, s_ids, p.ids_out, p.w_out);
 }
 
-// Down sweep.  The work is the row space of "segments": a segment is one
-// union slot and a group of up to kGroup of the rows that use it (a slot used
-// by more rows than that is swept once per group).  Every wave takes an equal
-// contiguous share of segments x h output rows -- at most two segments -- so
-// waves never wait for each other.  A wave holds its group's act rows in
-// registers (loaded once per segment) and loads its next batch of weight rows
-// while it computes the current batch.  For row r of union slot u, with
-// pair t the (row, expert) pair of (u, r):
+// Down sweep.  The work is one "segment" per union slot (and one for the
+// shared expert): the slot's down matrix times the act rows of every row that
+// uses it.  A wave holds up to kGroup act rows in registers (loaded once per
+// segment), so a slot used by more rows is swept by several row groups side
+// by side (see the wave mapping below).  Each wave loads its next batches of
+// weight rows while it computes the current one.  For row r of union slot u,
+// with pair t the (row, expert) pair of (u, r):
 //   y[t][n] = W_down[u][n,:] . act[t][:]
 constexpr int kDownThreads = 256;
 constexpr int kDownBatch = 4;  // weight rows per prefetch batch (stored as float4s)
@@ -204,7 +203,7 @@ struct DownBatch {
 
 template <int NCH>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
-  constexpr int kGroup = kDownGroup;  // act rows held per segment (16 VGPRs each per 2048 columns)
+  constexpr int kGroup = down_group(NCH);  // act rows a wave holds (the segment table's group size)
   constexpr int kMaxSegs = kMaxDownSegs;
   static_assert(kMaxSegs < 256, "the segment search spans at most 255 segments");
   __shared__ SlotInfo s_slots[kNumSlots];
