@@ -42,20 +42,23 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed-MoE layer µs/step + achieved HBM GB/s (% peak), rows=1..8, NVFP4"
 
-# HBM bytes per dispatch of the gate/up sweep at rows=8, measured with rocprofv3 --pmc
-# (FETCH_SIZE x 2.000 + WRITE_SIZE; the factor comes from a plain 1 GiB copy, see
-# profiles/moe_forward_e256_rows8_pmc.md).  Valid only for the kernel sources it was taken on.
-TRAFFIC_SOURCES = ("mixture_experts_decode_gate_amd/csrc/moe_kernels.hip",
-                   "mixture_experts_decode_gate_amd/csrc/moe_device.h")
-TRAFFIC_MEASURED = {"sources_sha256_16": "0fa4d9085a164c4f", "rows": 8, "gate_up_sweep_bytes": 794_587_167}
+# HBM traffic of the gate/up sweep at rows=8 per algorithmic byte, measured with
+# rocprofv3 --pmc over 125 dispatches (FETCH_SIZE x 2.000 + WRITE_SIZE; the factor comes
+# from a plain 1 GiB copy, see profiles/gateup_sweep_e256_rows1_2_4_8_pmc.md).  Valid only
+# for the kernel sources it was taken on; the roofline's traffic is this ratio times the
+# launch's algorithmic bytes.
+TRAFFIC_SOURCES = ('mixture_experts_decode_gate_amd/csrc/moe_gateup.h', 'mixture_experts_decode_gate_amd/csrc/moe_common.h',
+                   'mixture_experts_decode_gate_amd/csrc/moe_device.h', 'mixture_experts_decode_gate_amd/csrc/moe_gateup_rows_5_8.hip')
+TRAFFIC_MEASURED = {"sources_sha256_16": "06ee97d9667d47b4", "rows": 8, "gate_up_traffic_per_byte": 1.0050}
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "c4_e256_prefill8"
 N_INPUTS = 16
 
 
-def measured_traffic(rows: int):
-    """Counter-measured bytes per launch of the dominant kernel, or None when the
-    kernel sources changed since the counters were taken."""
+def measured_traffic(rows: int, bytes_per_launch: float):
+    """Counter-measured HBM bytes per launch of the dominant kernel (the measured
+    traffic per algorithmic byte times this launch's algorithmic bytes), or None
+    when the kernel sources changed since the counters were taken."""
     import hashlib
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
@@ -63,7 +66,7 @@ def measured_traffic(rows: int):
             h.update(fh.read())
     if h.hexdigest()[:16] != TRAFFIC_MEASURED["sources_sha256_16"] or rows != TRAFFIC_MEASURED["rows"]:
         return None
-    return TRAFFIC_MEASURED["gate_up_sweep_bytes"]
+    return int(round(TRAFFIC_MEASURED["gate_up_traffic_per_byte"] * bytes_per_launch))
 
 
 def log(*a):
@@ -580,7 +583,7 @@ def main():
                    "mean_union": res["mean_union"]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(st["gbps"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(st["gbps"] / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(args.rows),
+                     "traffic": measured_traffic(args.rows, st["bytes_per_launch"]),
                      "avg_launch_us": round(st["avg_us"], 2), "bytes_per_launch": int(st["bytes_per_launch"]),
                      "timed_launches": st["launches"],
                      "timing": "kernel start/stop events (hipExtLaunchKernel) in a second pass of the same steps"},
