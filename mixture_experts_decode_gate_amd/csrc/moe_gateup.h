@@ -201,7 +201,9 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   __syncthreads();
   if (wave == 0) {
     UnionLane ul;
-    if (p.token_major)
+    // One row's top-k ids are distinct and already in first-occurrence order:
+    // its union over the full expert range is the slot list itself.
+    if (p.token_major || (R == 1 && rp.expert_lo == 0 && rp.expert_hi >= rp.E))
       identity_slots(s_ids, R * rp.k, rp.k, lane, s_uids, &s_union, s_s2u, s_rmask, ul);
     else
       union_wave(s_ids, R * rp.k, rp.k, R, rp.expert_lo, rp.expert_hi, lane, s_uids, &s_union, s_s2u, s_rmask, ul);
