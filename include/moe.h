@@ -20,9 +20,11 @@
  *   packed codes, scales and scale2 values.
  *
  *   "Function forward_moe" rustdoc, "RETRACTED (2026-08-29)" and
- *   "WIDENED (2026-08-31)" notes: the top_k*rows <= 64 selected ids are
- *   deduplicated in one block by a pairwise scan (no sort), and each expert
- *   of the union is swept once for all rows that chose it; rows <= 8.
+ *   "WIDENED (2026-08-31)" notes: the selected ids are deduplicated in one
+ *   block by a pairwise scan (no sort), and each expert of the union is
+ *   swept once for all rows that chose it.  The pages' block holds
+ *   top_k*rows <= 64 ids (8 rows x 8); here the same scan runs over up to
+ *   two 64-slot tiles, so one call takes up to 16 rows and 128 ids.
  *   SHARED-expert note: the shared expert runs once over all rows.
  *
  * Per row r:
@@ -84,7 +86,7 @@ typedef enum moe_status {
 enum {
   MOE_ROUTE_SOFTMAX = 0,      /* softmax top-k, optional renormalisation        */
   MOE_ROUTE_SIGMOID_BIAS = 1, /* sigmoid + correction bias, routed_scaling_factor */
-  MOE_MAX_ROWS = 16,          /* rows per call (MOE_BLOCK_IDS ids in one wave tile) */
+  MOE_MAX_ROWS = 16,          /* rows per call                                   */
   MOE_MAX_IDS = 128,          /* top_k * rows, two tiles of MOE_BLOCK_IDS         */
   MOE_BLOCK_IDS = 64,         /* the one-block union of the "RETRACTED (2026-08-29)"
                                  and "WIDENED (2026-08-31)" notes: 8 rows x 8    */

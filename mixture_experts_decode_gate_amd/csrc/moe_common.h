@@ -283,8 +283,8 @@ __device__ void topk_select(const RouteParams& p, int r, int lane, TopkIn<G>& in
 }
 
 // ---------------------------------------------------------------- sweeps
-// Copy the slot table into LDS (all 65 entries: those past U are stale and
-// never read, and not waiting for U saves a round trip).  Later reads come
+// Copy the slot table into LDS (all kNumSlots entries: those past U are stale
+// and never read, and not waiting for U saves a round trip).  Later reads come
 // from LDS: a global load issued after the prefetched weights would make the
 // in-order load counter drain the prefetch.  Each thread issues all its loads
 // before its first store, so the copy costs one memory round trip, not one

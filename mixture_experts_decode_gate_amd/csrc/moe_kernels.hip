@@ -250,9 +250,9 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   // virtual wave v of V works on the segment s with c_s <= v * C / V <
   // c_{s+1}.  Within a segment of G row groups, consecutive virtual waves take
   // groups 0, 1, .., G-1 of the same batch: the waves that read a weight row
-  // for the slot's different row groups sit side by side (the shared slot,
-  // first, starts at wave 0, so at 8 rows its four groups share each block)
-  // and the repeated reads are served by the cache.  Each group's waves take
+  // for the slot's different row groups sit side by side (the shared slot
+  // comes first and starts at wave 0, so its groups share a block) and the
+  // repeated reads are served by the cache.  Each group's waves take
   // interleaved batches of kDownBatch rows: every group sweeps its matrix
   // front to back together.  V >= C gives every segment at least 4 G virtual
   // waves (a segment weighs at least 4 per group); with fewer waves than that
