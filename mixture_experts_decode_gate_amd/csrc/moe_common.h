@@ -19,10 +19,12 @@ namespace moe {
 //
 // Block e (of E+1) computes router row e for every input row (e == E is the
 // shared expert's gate vector): wave c < nkc takes the kRouterChunk-column
-// chunk c, issues all its loads before any arithmetic, accumulates in fp64
-// and reduces in a fixed order; the chunk partials are summed in chunk order
-// and rounded once: logits[r][e] = fp32(sum), gamma[r] = fp32(sigmoid(sum)),
-// and for sigmoid routing score[r][e] = sigmoid(sum) in fp64.
+// chunk c, issues all its loads before any arithmetic and accumulates in
+// fp64.  The sum runs in a fixed order that does not depend on the number of
+// rows: each quad of lanes per chunk, those partials in chunk order, then the
+// 16 quads; it is rounded once: logits[r][e] = fp32(sum),
+// gamma[r] = fp32(sigmoid(sum)), and for sigmoid routing
+// score[r][e] = sigmoid(fp32(sum)) in fp64.
 constexpr int kRouterChunk = 512;
 constexpr int kMaxRouterChunks = MOE_MAX_DIM / kRouterChunk;
 constexpr int kRouteThreads = 64 * kMaxRouterChunks;  // a wave per router chunk

@@ -152,6 +152,27 @@ __device__ __forceinline__ void wave_sum_n(double (&v)[N]) {
   }
 }
 
+// The first two steps of wave_sum(double) on N independent values: every lane
+// of a quad ends with the quad's sum (both additions are commutative, so the
+// four lanes hold the same bits).
+template <int N>
+__device__ __forceinline__ void quad_sum_n(double (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f64<0xB1, 0xF>(v[i]);  // quad_perm [1,0,3,2]
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f64<0x4E, 0xF>(v[i]);  // quad_perm [2,3,0,1]
+}
+
+// Sum over each DPP row of 16 lanes (the first four steps of wave_sum):
+// every lane of the row ends with the row's sum.
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_f64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_f64<0x140, 0xF>(v);  // row_mirror
+  return v;
+}
+
 // Maximum over the 64 lanes (same DPP pattern as wave_sum; lanes a step
 // does not reach read 0, the identity), returned to every lane.
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {

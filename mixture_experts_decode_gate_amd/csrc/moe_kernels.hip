@@ -111,7 +111,8 @@ __device__ __forceinline__ void router_dot_nvfp4(const RouteParams& p, int e, in
 
 template <int R>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
-  __shared__ double part[kMaxRouterChunks][kMaxRows];
+  // part[c][r][q]: chunk c's partial for row r over the quad of lanes 4q..4q+3
+  __shared__ double part[kMaxRouterChunks][R][16];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int h = p.h, E = p.E;
@@ -125,47 +126,38 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteParams p) {
       router_dot_nvfp4<R>(p, e, c, lane, acc);
     else
       router_dot_f32<R>(p, (e < E) ? p.router_w + (size_t)e * h : p.gate_vec, c, lane, acc);
-    wave_sum_n<R>(acc);
-    if (lane == 0) {
+    quad_sum_n<R>(acc);
+    if ((lane & 3) == 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) part[c][r] = acc[r];
+      for (int r = 0; r < R; ++r) part[c][r][lane >> 2] = acc[r];
     }
   }
   __syncthreads();
-  // Wave 0: lane r sums row r's chunk partials in chunk order and takes the
-  // sigmoid (the gate row always; router rows for sigmoid routing), and lane
-  // 0 writes every row's results.  The kernel that follows reads them after
+  // Thread 16r + q finishes quad q of row r: its chunk partials summed in
+  // chunk order, then the row's 16 quads reduced across its DPP row (row r
+  // sits on lanes 16(r % 4) .. +15 of wave r / 4).  The row's first lane
+  // takes the sigmoid (the gate row always; router rows for sigmoid routing)
+  // and writes the row's results; the kernel that follows reads them after
   // the kernel boundary.
-  if (wave == 0) {
-    double z = 0.0, sg = 0.0;
-    if (lane < R) {
-      for (int cc = 0; cc < nkc; ++cc) z += part[cc][lane];
+  if ((int)threadIdx.x < 16 * R) {
+    const int r = (int)threadIdx.x >> 4, q = (int)threadIdx.x & 15;
+    double v[kMaxRouterChunks];
+#pragma unroll
+    for (int cc = 0; cc < kMaxRouterChunks; ++cc) v[cc] = part[cc < nkc ? cc : 0][r][q];
+    double z = v[0];
+#pragma unroll
+    for (int cc = 1; cc < kMaxRouterChunks; ++cc)
+      if (cc < nkc) z += v[cc];
+    z = row16_sum(z);
+    if (q == 0) {
       if (p.router_fp4 && e < E) z *= (double)p.router_scale2;
       // The gate takes the fp64 sum; routing scores take the fp32 logit, the
       // value top-k sees.
-      if (e == E)
-        sg = p.ungated ? 1.0 : 1.0 / (1.0 + exp(-z));
-      else if (p.route_kind == MOE_ROUTE_SIGMOID_BIAS)
-        sg = 1.0 / (1.0 + exp(-(double)(float)z));
-    }
-    double zr[R], sr[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint64_t zb = __builtin_bit_cast(uint64_t, z), sb = __builtin_bit_cast(uint64_t, sg);
-      zr[r] = __builtin_bit_cast(double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(zb >> 32), r) << 32) |
-                                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)zb, r));
-      sr[r] = __builtin_bit_cast(double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(sb >> 32), r) << 32) |
-                                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sb, r));
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (e < E) {
-          p.logits[r * E + e] = (float)zr[r];
-          p.score[r * E + e] = sr[r];
-        } else {
-          p.gamma[r] = (float)sr[r];
-        }
+      if (e < E) {
+        p.logits[r * E + e] = (float)z;
+        p.score[r * E + e] = p.route_kind == MOE_ROUTE_SIGMOID_BIAS ? 1.0 / (1.0 + exp(-(double)(float)z)) : 0.0;
+      } else {
+        p.gamma[r] = p.ungated ? 1.0f : (float)(1.0 / (1.0 + exp(-z)));
       }
     }
   }
