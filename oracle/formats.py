@@ -7,9 +7,9 @@ Pinned by tests/test_oracle_formats.py:
 * NVFP4 layout against hand-decoded bytes (tests/golden/nvfp4_layout.txt)
   and closed-form all-ones / one-hot matrices.
 
-The pages only name the weight format "NVFP4" (``forward_token_major.rs``:
-"untransposed NVFP4 experts", pointer tables of packed codes, scales and
-``scale2`` values).  The readings used here: a projection [n, k] is stored
+The pages only name the weight format NVFP4 (the token-major page serves its
+NVFP4 experts untransposed, through pointer tables of packed codes, scales
+and ``scale2`` values).  The readings used here: a projection [n, k] is stored
 K-contiguous ("untransposed"), two E2M1 codes per byte with the even column in
 the low nibble, one E4M3FN scale per 16 consecutive columns in a row-major
 [n, k/16] array, and one fp32 per-tensor ``scale2``.

@@ -18,7 +18,7 @@ with the j-sum in float64 in ascending j, gamma_r = sigmoid(x_r . g_s)
 
 Because every row is computed alone, deduplicating experts across rows cannot
 change any row's result ("Function forward_moe" rustdoc, "RETRACTED
-(2026-08-29)" note: outputs byte-identical either way).  The loop below
+(2026-08-29)" note: the same output bytes with or without the union).  The loop below
 groups (row, expert) pairs by expert only so an expert is decoded once; each
 pair's value is the same as if computed alone.
 """

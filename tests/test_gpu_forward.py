@@ -8,8 +8,8 @@
   outputs against a float64 recomputation from the kernel's own activations;
 * ragged shapes (partial 2048-column chunks), top_k = E, 64 ids;
 * a call with R rows equals R one-row calls byte for byte ("Function
-  forward_moe" rustdoc, "RETRACTED (2026-08-29)" note: byte-identical either
-  way); two runs are identical; a captured HIP graph replays identically.
+  forward_moe" rustdoc, "RETRACTED (2026-08-29)" note: the same output bytes
+  with or without the union); two runs are identical; a captured HIP graph replays identically.
 """
 
 import dataclasses

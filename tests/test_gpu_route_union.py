@@ -57,8 +57,8 @@ class RouteWeights:
         torch.cuda.synchronize()
         L = moe.moe_workspace_layout(self.cfg)
         E = self.shape.num_experts
-        logits = ws_read(ws, L.logits, np.float32, 8 * E).reshape(8, E)[:R]
-        gamma = ws_read(ws, L.gamma, np.float32, 8)[:R]
+        logits = ws_read(ws, L.logits, np.float32, R * E).reshape(R, E)
+        gamma = ws_read(ws, L.gamma, np.float32, R)
         return ids.cpu().numpy(), wts.cpu().numpy(), logits, gamma
 
 
@@ -93,8 +93,26 @@ def test_route_rows_256_experts(rows):
     check_route(rw, synth.activations(shape, 11, rows=rows))
 
 
+@pytest.mark.parametrize("name,max_rows", [("c4_e256_prefill8", 12), ("c2_e128_verify2", 16)])
+def test_route_rows_match_one_row_calls(name, max_rows):
+    # A row's logits, gate, ids and weights do not depend on the other rows
+    # of the call: the router sums each row in one fixed order for any row
+    # count, so R rows give the bytes of R one-row calls.  Up to the most rows
+    # a call takes at that hidden size (12 at 6144, MOE_MAX_ROWS = 16 at 4096).
+    shape = synth.CONFIGS[name]
+    rw = RouteWeights(shape)
+    x = synth.activations(shape, 13, rows=max_rows)
+    singles = [rw.run(x[r:r + 1]) for r in range(max_rows)]
+    for R in sorted({2, 3, 5, 8, max_rows}):
+        got = rw.run(x[:R])
+        for r in range(R):
+            for a, b in zip(got, singles[r]):
+                assert np.array_equal(a[r], b[0]), f"rows={R} row={r}"
+    check_route(rw, x)
+
+
 def test_route_largest_shape():
-    # MOE_MAX_DIM columns (8 router chunks, one per wave) and MOE_MAX_EXPERTS experts
+    # MOE_MAX_DIM columns (16 router chunks, one per wave) and MOE_MAX_EXPERTS experts
     shape = synth.MoeShape("max", 8192, 1024, 8, 64, 64, 8, synth.ROUTE_SIGMOID_BIAS, True, 2.5)
     rw = RouteWeights(shape)
     check_route(rw, synth.activations(shape, 3))
