@@ -16,11 +16,16 @@ steps.  A second pass of K steps launches every kernel with its own start and
 stop events (hipExtLaunchKernel: the kernel's own execution, nothing
 enqueued between kernels) and gives each stage's average kernel duration: the
 dominant kernel's roofline figure.  Also reports, in the same line:
+  staged_pass_per_step  p10 / median / p90 of each step's device time (first
+                        kernel start to last kernel stop) and GB/s in that pass
+                        (above us_per_step: its events widen the kernel gaps)
   sweep                 rows=1..8 at the same shape
   configs               every layer configuration at its own rows (also replayed
                         from a captured HIP graph: device time without launch cost)
   union_vs_token_major  the union sweep against moe_forward_token_major on the
                         same inputs (independent rows 1..8, correlated K=2..4)
+  union_past_8_rows_vs_8_row_sub_chunks
+                        12 and 16 rows in one union against 8-row sub-chunks
   ep_share              one GPU's expert-parallel share (8 ranges of 32 experts)
   read_ceiling_gbps     moe_read_probe's streaming-read rate over 4 GiB
   cpu_baseline          the CPU oracle timed on a bounded sample (a reference
@@ -198,6 +203,13 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, stage_events=
             stage[name] = dict(avg_us=float(np.mean(d)) * 1e3, gbps=b / (sum(d) * 1e-3) / 1e9,
                                bytes_per_launch=b / len(traced), launches=len(traced))
         res["stages"] = stage
+        # Per step: the first kernel's start to the last kernel's stop (device
+        # time of the whole step), and the GB/s of that step's own bytes.
+        step_us = np.array([events[i][0].elapsed_ms(events[i][2 * nst - 1]) * 1e3 for i in traced])
+        step_gbps = np.array([sbytes[i]["layer"] for i in traced]) / (step_us * 1e-6) / 1e9
+        res["per_step"] = dict(us_p10_p50_p90=[round(float(v), 2) for v in np.percentile(step_us, [10, 50, 90])],
+                               gbps_p10_p50_p90=[round(float(v), 1) for v in np.percentile(step_gbps, [10, 50, 90])],
+                               steps=len(traced))
     return res
 
 
@@ -590,6 +602,10 @@ def main():
         "stages_us": {k: round(v["avg_us"], 2) for k, v in staged["stages"].items()},
         "stages_gbps": {k: round(v["gbps"], 1) for k, v in staged["stages"].items()},
         "staged_pass_us_per_step": round(staged["us_per_step"], 2),
+        "staged_pass_per_step": dict(staged["per_step"],
+                                     timing="first kernel start to last kernel stop of each step in the "
+                                            "event-timed pass (its event records widen the gaps between "
+                                            "kernels, so these read above us_per_step)"),
         "copy_gbps": round(copy_gbps, 1),
         "read_ceiling_gbps": round(read_gbps, 1),
         "pct_of_read_ceiling": round(100 * res["gbps"] / read_gbps, 2),
