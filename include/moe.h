@@ -187,6 +187,8 @@ moe_status moe_workspace_layout(const moe_config* cfg, moe_ws_layout* out);
  * moe_topk_sigmoid_batched or moe_topk_softmax_batched; forward_ep.rs: the
  * one-row GEMV and moe_topk_softmax).
  *   x_bf16    [rows, h] bf16 bits, 16-byte aligned
+ *   rows      1 .. MOE_MAX_ROWS with top_k * rows <= MOE_MAX_IDS, at any
+ *             hidden size (the router stages no x; moe_forward may take fewer)
  *   topk_ids  [rows, k] int32 out, ordered by descending key, ties by lower id
  *   topk_w    [rows, k] fp32 out
  * Also leaves logits and gamma in the workspace. */

@@ -94,12 +94,20 @@ int max_rows(const moe_config* c) {
   return r;
 }
 
-moe_status check_rows(const moe_config* c, int32_t rows) {
+// Rows routing alone takes: MOE_MAX_ROWS, and top_k * rows ids for the union.
+moe_status check_route_rows(const moe_config* c, int32_t rows) {
   if (rows < 1 || rows > MOE_MAX_ROWS)
     return fail(MOE_ERR_INVALID_ARG, "rows=%d outside [1, %d]", rows, MOE_MAX_ROWS);
   if (c->top_k * rows > MOE_MAX_IDS)
     return fail(MOE_ERR_INVALID_ARG, "top_k*rows=%d exceeds the %d ids the union takes", c->top_k * rows,
                 MOE_MAX_IDS);
+  return MOE_OK;
+}
+
+// Rows the whole layer takes: also every row of x in the gate/up sweep's LDS.
+moe_status check_rows(const moe_config* c, int32_t rows) {
+  moe_status st = check_route_rows(c, rows);
+  if (st) return st;
   if (rows * x_chunks(c) > MOE_MAX_CHUNK_ROWS)
     return fail(MOE_ERR_UNSUPPORTED,
                 "rows=%d at hidden=%d stages %d chunks of x in LDS (at most %d): at most %d rows per call here; "
@@ -419,7 +427,7 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const uint16_t
                      int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_config(cfg);
   if (st) return st;
-  if ((st = check_rows(cfg, rows))) return st;
+  if ((st = check_route_rows(cfg, rows))) return st;
   if ((st = check_route_weights(cfg, w))) return st;
   moe_ws_layout L;
   if ((st = check_ws(cfg, ws, ws_bytes, &L))) return st;

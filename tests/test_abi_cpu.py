@@ -169,6 +169,10 @@ def test_route_refusals():
     assert r(0, OUT) == moe.MOE_ERR_INVALID_ARG
     assert r(OUT, OUT + 16) == moe.MOE_ERR_INVALID_ARG   # ids and weights overlap
     assert r(OUT, OUT + 4096, rows=17) == moe.MOE_ERR_INVALID_ARG
+    big = cfg_c4(top_k=16)
+    assert lib.moe_route(ctypes.byref(big), ctypes.byref(fake_weights()), X, 9, OUT, OUT + 4096, WS,
+                         lib.moe_workspace_bytes(ctypes.byref(big)), None) == moe.MOE_ERR_INVALID_ARG
+    assert "128" in lib.moe_last_error().decode()  # top_k * rows past the union's ids
 
 
 def test_stage_names():

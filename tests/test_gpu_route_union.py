@@ -93,12 +93,12 @@ def test_route_rows_256_experts(rows):
     check_route(rw, synth.activations(shape, 11, rows=rows))
 
 
-@pytest.mark.parametrize("name,max_rows", [("c4_e256_prefill8", 12), ("c2_e128_verify2", 16)])
+@pytest.mark.parametrize("name,max_rows", [("c4_e256_prefill8", 16), ("c2_e128_verify2", 16)])
 def test_route_rows_match_one_row_calls(name, max_rows):
     # A row's logits, gate, ids and weights do not depend on the other rows
     # of the call: the router sums each row in one fixed order for any row
-    # count, so R rows give the bytes of R one-row calls.  Up to the most rows
-    # a call takes at that hidden size (12 at 6144, MOE_MAX_ROWS = 16 at 4096).
+    # count, so R rows give the bytes of R one-row calls, up to MOE_MAX_ROWS
+    # (routing alone takes 16 rows at any hidden size).
     shape = synth.CONFIGS[name]
     rw = RouteWeights(shape)
     x = synth.activations(shape, 13, rows=max_rows)
