@@ -153,6 +153,33 @@ def test_rows_equal_one_row_calls_256(layer256):
         assert np.array_equal(got, singles[:R]), f"rows={R}"
 
 
+def test_concurrent_calls_on_two_streams():
+    # Calls on different streams, each with its own workspace, share no state:
+    # interleaved on two streams (kernels of both in flight together), they
+    # give the bytes of the same calls made one at a time, and so does the
+    # token-major path.
+    torch = torch_cuda()
+    moe = moe_mod()
+    shape = synth.CONFIGS["c2_e128_verify2"]
+    dl = upload(synth.layer_weights(shape))
+    xb = [synth.activations(shape, s) for s in range(4)]
+    want = [run_forward(dl, x)[0] for x in xb]
+    xs = [x_dev(x) for x in xb]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [ws_for(dl.cfg), ws_for(dl.cfg)]
+    for fwd in (moe.moe_forward, moe.moe_forward_token_major):
+        outs = [torch.zeros_like(x) for x in xs]
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for s in range(4):
+                st = streams[s % 2]
+                with torch.cuda.stream(st):
+                    fwd(dl.cfg, dl.weights, xs[s], outs[s], wss[s % 2], stream=st)
+        torch.cuda.synchronize()
+        for s in range(4):
+            assert np.array_equal(out_bits(outs[s]), want[s]), (fwd.__name__, s)
+
+
 def test_deterministic_256(layer256):
     _, dl = layer256
     x = synth.activations(synth.CONFIGS["c4_e256_prefill8"], 5)
