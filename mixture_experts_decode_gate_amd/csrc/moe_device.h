@@ -152,6 +152,41 @@ __device__ __forceinline__ void wave_sum_n(double (&v)[N]) {
   }
 }
 
+// Lane moves past a quad: ds_swizzle in bit-mask mode (lane l reads lane
+// l ^ M within its 32-lane half) and ds_bpermute (lane l reads lane l ^ 32).
+template <int M>
+__device__ __forceinline__ float swizzle_xor(float v) {
+  static_assert(M > 0 && M < 32, "ds_swizzle exchanges within 32 lanes");
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), (M << 10) | 0x1F));
+}
+__device__ __forceinline__ float xor32_lane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, v)));
+}
+
+// Sum over the 64 lanes of four values at once: lane l ends with the total of
+// value sum4_value(l) = 2 (l & 1) + ((l >> 1) & 1).  Across lane pairs each
+// lane keeps two of the values and receives the partner's copy of them, across
+// quads one; the remaining steps are a butterfly on that one value (lanes
+// l ^ 4, 8, 16, 32).  Each value's additions form the same xor tree over the
+// lanes whatever the other values hold, and every lane with the same value
+// index ends with the same bits.
+__device__ __forceinline__ int sum4_value(int lane) { return 2 * (lane & 1) + ((lane >> 1) & 1); }
+
+__device__ __forceinline__ float wave_sum4_scatter(const float (&v)[4], int lane) {
+  const bool p = lane & 1, q = lane & 2;
+  const float k0 = p ? v[2] : v[0], k1 = p ? v[3] : v[1];
+  const float s0 = p ? v[0] : v[2], s1 = p ? v[1] : v[3];
+  const float a0 = k0 + __builtin_bit_cast(float, dpp_u32<0xB1, 0xF>(__builtin_bit_cast(uint32_t, s0)));
+  const float a1 = k1 + __builtin_bit_cast(float, dpp_u32<0xB1, 0xF>(__builtin_bit_cast(uint32_t, s1)));
+  const float kq = q ? a1 : a0, sq = q ? a0 : a1;
+  float b = kq + __builtin_bit_cast(float, dpp_u32<0x4E, 0xF>(__builtin_bit_cast(uint32_t, sq)));
+  b += swizzle_xor<4>(b);
+  b += swizzle_xor<8>(b);
+  b += swizzle_xor<16>(b);
+  b += xor32_lane(b, lane);
+  return b;
+}
+
 // The first two steps of wave_sum(double) on N independent values: every lane
 // of a quad ends with the quad's sum (both additions are commutative, so the
 // four lanes hold the same bits).

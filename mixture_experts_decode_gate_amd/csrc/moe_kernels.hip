@@ -353,22 +353,9 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
 #pragma unroll
       for (int g = 0; g < kGroup; ++g) {
         if (g < cnt) {
-          wave_sum_n<kDownBatch>(acc[g]);
-          float* dst = p.y + (size_t)prs[g] * h + nb;
-          if (lane == 0) {
-
-#pragma unroll
-            for (int i = 0; i < kDownBatch; i += 4) {
-              if (nb + i + 4 <= n_end) {
-                *reinterpret_cast<float4*>(dst + i) =
-                    make_float4(acc[g][i] * d2, acc[g][i + 1] * d2, acc[g][i + 2] * d2, acc[g][i + 3] * d2);
-              } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                  if (nb + i + q < n_end) dst[i + q] = acc[g][i + q] * d2;
-              }
-            }
-          }
+          const float t = wave_sum4_scatter(acc[g], lane);
+          const int j = sum4_value(lane);
+          if (lane < kDownBatch && nb + j < n_end) p.y[(size_t)prs[g] * h + nb + j] = t * d2;
         }
       }
     };
@@ -421,9 +408,12 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
 // blend_kernel's order, so both paths write the same bytes; y is also written
 // to the workspace.  Work units are (slot, batch of kDownBatch output rows),
 // the shared expert's first; the block's waves claim them from an LDS counter
-// and keep two units in flight while they compute one.
+// and keep two units in flight while they compute one.  It serves one or two
+// rows: with more, the registers of 12 waves per CU no longer hold two rows'
+// activations beside three weight batches, and the down sweep + blend kernels
+// take over.
 constexpr int kDbThreads = 768;  // 12 waves, one block per CU
-constexpr int kDbMaxRows = 4;    // rows served by this kernel (act of every pair in LDS)
+constexpr int kDbMaxRows = 2;    // rows served by this kernel (act of every pair in LDS)
 constexpr int kDbActPer = 12;    // act staging loads per thread (16 bytes each)
 
 template <int R, int NCH>
@@ -443,14 +433,11 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
   const int n_begin = blockIdx.x * nr;
   const int nbat = nr / kDownBatch;
 
-  // Prologue, in three steps so the first weight loads go out early: (1) the
-  // slot table, U, routing weights and gates, then a shared-expert unit's
-  // weights (their pointers are this kernel's arguments); (2) once the slot
-  // table is in LDS, the first routed unit's weights; (3) the act rows, staged
-  // while those weights are in flight.  With one or two rows the act rows are
-  // few and go out with step (1) instead, saving a round trip.  Loads are
-  // consumed in issue order.
-  constexpr bool kActFirst = R <= 2;
+  // Prologue, in two steps so the first weight loads go out early: (1) the
+  // slot table, U, routing weights and gates and every act row, then a
+  // shared-expert unit's weights (their pointers are this kernel's
+  // arguments); (2) once the slot table is in LDS, the first routed unit's
+  // weights.  Loads are consumed in issue order.
   const int units = P * NCH * kChunkUnits;
   // Unit i of the act staging is 16 bytes of pair t, chunk c, unit un
   // (columns past the pair's K read a valid copy and are stored as zeros).
@@ -500,8 +487,8 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
   const float wv = ld_global(rp.w_out + tw);
   const int s2u = ld_global(rp.slot_to_union + tw);
   const float gv = ld_global(rp.gamma + ((int)threadIdx.x < R ? (int)threadIdx.x : 0));
-  u32x4 av_first[kActFirst ? kDbActPer : 1];
-  if (kActFirst) act_issue(av_first, 0, kDbActPer);
+  u32x4 av_first[kDbActPer];
+  act_issue(av_first, 0, kDbActPer);
   if (threadIdx.x == 0) {
     s_next = 0;
     s_slots[kSharedSlot] = shared_slot_info(rp, (1u << R) - 1u);
@@ -568,7 +555,7 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
     if ((int)threadIdx.x < R) s_gamma[threadIdx.x] = gv;
 #pragma unroll
     for (int q = 0; q < kTabPer; ++q) asm volatile("" ::"v"(tab[q]));
-    if (kActFirst) act_store(av_first, 0, kDbActPer);
+    act_store(av_first, 0, kDbActPer);
   }
   __syncthreads();
   const int total = (s_union + 1) * nbat;
@@ -586,21 +573,8 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
   }
   fetch(id_b, bb, ib);
 
-  // Step (3): the act rows, in passes of kActPass loads per thread (two at
-  // most: the launcher serves this kernel only when kDbActPer loads per
-  // thread cover every unit).
-  if (!kActFirst) {
-    constexpr int kActPass = kDbActPer / 2;
-    for (int base = 0; base < units; base += kActPass * kDbThreads) {
-      u32x4 av[kActPass];
-      act_issue(av, base, kActPass);
-      act_store(av, base, kActPass);
-    }
-    __syncthreads();
-  }
-
-  // Rows of a unit in groups of two (act rows from LDS), each weight row
-  // decoded once per group; y to LDS and the workspace.
+  // The unit's one or two rows (act rows from LDS), each weight row decoded
+  // once; y to LDS and the workspace.
   auto compute = [&](const DownBatch<NCH>& b, const UnitInfo& ui) {
 #pragma unroll
     for (int g = 0; g < (R + 1) / 2; ++g) {
@@ -635,28 +609,19 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
           if (u0) acc0[i] = dot32(dw, x0[c][0], x0[c][1], x0[c][2], x0[c][3], s0, s1, acc0[i]);
           if (u1) acc1[i] = dot32(dw, x1[c][0], x1[c][1], x1[c][2], x1[c][3], s0, s1, acc1[i]);
         }
-        // with two groups, one weight row decoded at a time keeps the kernel
-        // within the 168 registers of 12 waves per CU
-        if (R > 2) __builtin_amdgcn_sched_barrier(0);
       }
       auto emit = [&](float (&acc)[kDownBatch], int pr) {
-        wave_sum_n<kDownBatch>(acc);
-        if (lane == 0) {
-          const int nl = ui.n - n_begin;
-          float* dst = p.y + (size_t)pr * h + ui.n;
-          if (ui.n + kDownBatch <= h) {
-            *reinterpret_cast<float4*>(dst) =
-                make_float4(acc[0] * ui.d2, acc[1] * ui.d2, acc[2] * ui.d2, acc[3] * ui.d2);
-          } else {
-#pragma unroll
-            for (int i = 0; i < kDownBatch; ++i)
-              if (ui.n + i < h) dst[i] = acc[i] * ui.d2;
-          }
-#pragma unroll
-          for (int i = 0; i < kDownBatch; ++i) s_y[pr * nr + nl + i] = acc[i] * ui.d2;
+        const float t = wave_sum4_scatter(acc, lane);
+        const int j = sum4_value(lane);
+        if (lane < kDownBatch) {
+          const float yv = t * ui.d2;
+          if (ui.n + j < h) p.y[(size_t)pr * h + ui.n + j] = yv;
+          s_y[pr * nr + (ui.n - n_begin) + j] = yv;
         }
       };
       if (u0) emit(acc0, p0);
+      // the two rows' sums one after the other: fewer registers live at once
+      __builtin_amdgcn_sched_barrier(0);
       if (u1) emit(acc1, p1);
       // the next group's act rows are read from LDS after this group is done
       __builtin_amdgcn_sched_barrier(0);
@@ -917,8 +882,6 @@ hipError_t launch_down_blend(const SweepParams& p, int rows, int nr, hipStream_t
   switch (rows) {
     case 1: return down_blend_r<1>(p, nr, s, ev);
     case 2: return down_blend_r<2>(p, nr, s, ev);
-    case 3: return down_blend_r<3>(p, nr, s, ev);
-    case 4: return down_blend_r<4>(p, nr, s, ev);
   }
   return hipErrorInvalidValue;
 }
