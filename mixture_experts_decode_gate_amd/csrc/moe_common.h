@@ -490,6 +490,17 @@ constexpr int kNumXcds = 8;  // accelerator dies; workgroups go to them round-ro
 constexpr int kProbeBlocksPerCU = 16;
 constexpr int kProbeUnroll = 16;
 
+// Workgroup b runs on XCD b % kNumXcds.  Its XCD-major index numbers the
+// blocks die by die (the blocks of one XCD get consecutive indices), so work
+// split by that index gives each die contiguous runs of weight rows rather
+// than every kNumXcds-th row, whose addresses can fall unevenly on the HBM
+// channels.  A bijection on [0, gridDim.x) when the grid is a multiple of
+// kNumXcds, the identity otherwise.
+__device__ __forceinline__ int xcd_major_block() {
+  const int nb = (int)gridDim.x, b = (int)blockIdx.x;
+  return nb % kNumXcds == 0 ? (b % kNumXcds) * (nb / kNumXcds) + b / kNumXcds : b;
+}
+
 inline int current_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;

@@ -15,9 +15,10 @@ namespace moe {
 //
 // Work items are rows n of each union slot's gate and up matrices (the shared
 // expert's Is rows first, then each routed slot's I rows).
-// Block b owns items b, b + B, b + 2B, ... (B blocks), so all blocks sweep
-// the weights front to back together; its waves claim the block's items in
-// order from a counter in LDS.  Waves that share a SIMD are not issued evenly
+// The block with XCD-major index v (xcd_major_block) owns items v, v + B,
+// v + 2B, ... (B blocks), so all blocks sweep the weights front to back
+// together, each die over contiguous runs of rows; its waves claim the
+// block's items in order from a counter in LDS.  Waves that share a SIMD are not issued evenly
 // (the oldest goes first): with claims, one that is issued less simply takes
 // fewer items, instead of finishing far behind its neighbours.  A claim is an
 // LDS atomic, tracked apart from the weight loads, so taking one never waits
@@ -111,13 +112,14 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   __syncthreads();
 
   // Items: the shared expert's Is rows first, then each routed slot's I rows.
-  // The item id of the block's claim i is b + i * B (not yet checked against
+  // The item id of the block's claim i is v + i * B (not yet checked against
   // the item count, which needs U).
+  const int vblock = xcd_major_block();
   auto claim_id = [&]() -> long long {
     int i = 0;
     if (lane == 0) i = atomicAdd(&s_next, 1);
     i = __builtin_amdgcn_readfirstlane(i);
-    return (long long)blockIdx.x + (long long)i * gridDim.x;
+    return (long long)vblock + (long long)i * gridDim.x;
   };
   // What the compute needs of an item's slot, in scalar registers: the rows
   // that use it, the per-tensor scales and each row's pair index (byte r).

@@ -254,11 +254,10 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
   const int C = s_seg_cum[nseg];
   const int V = W > C ? W : C;
 
-  // Workgroup b runs on XCD b % 8; numbering the blocks XCD by XCD gives each
-  // XCD (and its L2) a contiguous run of virtual waves, so the row groups of
-  // one slot and the readers of one act row mostly share an L2.
-  const int nb = (int)gridDim.x, b = (int)blockIdx.x;
-  const int lb = nb % kNumXcds == 0 ? (b % kNumXcds) * (nb / kNumXcds) + b / kNumXcds : b;
+  // Numbering the blocks XCD by XCD gives each XCD (and its L2) a contiguous
+  // run of virtual waves, so the row groups of one slot and the readers of one
+  // act row mostly share an L2.
+  const int lb = xcd_major_block();
 
   DownBatch<NCH> buf[kDownBufs];
   u32x4 act[kGroup][NCH][4];
@@ -397,9 +396,10 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
 
 // ---------------------------------------------------------------- down sweep + blend, few rows
 // With few rows the activations of every (row, expert) pair fit in LDS, and a
-// single kernel runs the down projections and the weighted sum.  Block b owns
-// output rows [b*nr, (b+1)*nr) of every union slot and of the shared expert,
-// so every term of out[r][n] is computed inside the block: the blend needs no
+// single kernel runs the down projections and the weighted sum.  The block
+// with XCD-major index v (xcd_major_block) owns output rows [v*nr, (v+1)*nr)
+// of every union slot and of the shared expert, so every term of out[r][n]
+// is computed inside the block: the blend needs no
 // kernel of its own and the expert outputs no round trip through memory.
 //   y[t][n]   = W_down[u][n,:] . act[t][:]        (t: the pair of slot u and row r)
 //   out[r][n] = bf16( sum_{j<k} w[r][j] * y[r*k + j][n] + gamma[r] * y[rows*k + r][n] )
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
   const int h = p.h, k = rp.k;
   const int P = R * k + R;  // pairs
   float* s_y = reinterpret_cast<float*>(s_act + (size_t)P * NCH * kChunkUnits);
-  const int n_begin = blockIdx.x * nr;
+  const int n_begin = xcd_major_block() * nr;
   const int nbat = nr / kDownBatch;
 
   // Prologue, in two steps so the first weight loads go out early: (1) the
