@@ -10,7 +10,7 @@ libmoe.so.  The names match the C ABI in include/moe.h:
     moe_forward(cfg, w, x, out, ws)                  the whole layer
     moe_forward_static(cfg, w, x, out)               the whole layer, library-held workspace (no allocation)
     moe_forward_token_major(cfg, w, x, out, ws)      the layer without the union (one slot per pair)
-    moe_forward_prefill(cfg, w, x, out, ws)          any number of rows, in 8-row sub-chunks
+    moe_forward_prefill(cfg, w, x, out, ws)          any number of rows, in sub-chunks of up to 16 rows
     moe_forward_timed(cfg, w, x, out, ws, events)    same, with per-stage events
     moe_read_probe(src, sink)                        streaming-read ceiling (measurement aid)
     moe_union_local(topk_ids, lo, hi, union_ids, union_count, slot_to_union, row_mask, num_experts)
@@ -179,7 +179,8 @@ def moe_route(cfg: MoeConfig, w: MoeWeights, x, topk_ids, topk_w, ws, stream=Non
 
 def moe_union(topk_ids, union_ids, union_count, slot_to_union, row_mask=None, num_experts: int = MOE_MAX_EXPERTS,
               stream=None) -> None:
-    """topk_ids [rows, k] int32 -> union_ids [64], union_count [1], slot_to_union [rows*k], row_mask [64]."""
+    """topk_ids [rows, k] int32 -> union_ids [MOE_MAX_IDS], union_count [1], slot_to_union [rows*k],
+    row_mask [MOE_MAX_IDS] (int32 / uint32 device tensors)."""
     rows, k = int(topk_ids.shape[0]), int(topk_ids.shape[1])
     _check(load().moe_union(_ptr(topk_ids), rows, k, int(num_experts), _ptr(union_ids), _ptr(union_count),
                             _ptr(slot_to_union), _ptr(row_mask), _stream(stream)))
@@ -198,7 +199,8 @@ def moe_forward_static(cfg: MoeConfig, w: MoeWeights, x, out, stream=None) -> No
 
 
 def moe_forward_prefill(cfg: MoeConfig, w: MoeWeights, x, out, ws, stream=None) -> None:
-    """x [rows, h] bf16 (any rows >= 1) -> out [rows, h] bf16, in 8-row sub-chunks."""
+    """x [rows, h] bf16 (any rows >= 1) -> out [rows, h] bf16, in sub-chunks of the most rows one
+    moe_forward takes for this config (up to MOE_MAX_ROWS)."""
     _check(load().moe_forward_prefill(ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), int(x.shape[0]),
                                       _ptr(ws), int(ws.numel() * ws.element_size()), _stream(stream)))
 
