@@ -213,7 +213,7 @@ def timed_run(cfg, layers, xs, us, shape, rows, steps, warmup, ws, stage_events=
     return res
 
 
-def union_vs_subchunks(cfg, layers, shape, K, steps, ws, sub_rows=8):
+def union_vs_subchunks(cfg, layers, shape, K, steps, ws, settle_ms, sub_rows=8):
     """K rows as one moe_forward (one union over all K rows' experts) against
     the same rows as sub-chunks of ``sub_rows`` rows, one moe_forward each
     (each sub-chunk dedups only its own experts).  Same inputs, same layer
@@ -242,7 +242,7 @@ def union_vs_subchunks(cfg, layers, shape, K, steps, ws, sub_rows=8):
     sh = int(torch.cuda.current_stream().cuda_stream)
     res = {}
     for mode in ("one_union", "sub_chunks"):
-        torch.cuda.synchronize()
+        settle(cfg, layers, xs, ws, settle_ms)
         for i in range(10):  # warm-up, back to back with the timed steps
             moe.moe_forward(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], out, ws)
         e0, e1 = HipEvent(), HipEvent()
@@ -263,7 +263,7 @@ def union_vs_subchunks(cfg, layers, shape, K, steps, ws, sub_rows=8):
                 expert_streams_saved=round(1 - np.mean(u_one) / np.mean(u_sub), 4))
 
 
-def config_runs(steps, main_shape, main_layers, main_cfg, ws_main):
+def config_runs(steps, main_shape, main_layers, main_cfg, ws_main, settle_ms):
     """µs/step and GB/s of moe_forward on each configuration at its own rows.
     Every layer is copied on the device until a pass over the copies moves more
     than 1 GB of the bytes a step touches, so steps read HBM rather than the
@@ -286,6 +286,7 @@ def config_runs(steps, main_shape, main_layers, main_cfg, ws_main):
             ws = torch.zeros(moe.moe_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
         xs = [torch.from_numpy(synth.activations(shape, s).view(np.int16)).cuda() for s in range(N_INPUTS)]
         us = union_sizes(cfg, layers, xs, ws)
+        settle(cfg, layers, xs, ws, settle_ms)
         r = timed_run(cfg, layers, xs, us, shape, shape.rows, steps, 10, ws)
         g_us = graph_step_us(cfg, layers, xs, ws)
         out.append(dict(config=name, rows=shape.rows, mean_union=round(r["mean_union"], 3), layer_copies=len(layers),
@@ -349,7 +350,7 @@ def read_ceiling(nbytes=4 << 30, reps=5):
     return nbytes / (ms * 1e-3) / 1e9
 
 
-def ep_shares(cfg, layers, xs, shape, rows, n_ranks, steps, ws):
+def ep_shares(cfg, layers, xs, shape, rows, n_ranks, steps, ws, settle_ms):
     """Time moe_forward_ep_partial for each of n_ranks equal expert ranges."""
     import torch
     import mixture_experts_decode_gate_amd as moe
@@ -366,10 +367,11 @@ def ep_shares(cfg, layers, xs, shape, rows, n_ranks, steps, ws):
             moe.moe_forward_ep_partial(cfg, layers[0].weights, x, partial, lo, hi, ws)
             torch.cuda.synchronize()
             us.append(int(ws[L.union_count:L.union_count + 4].cpu().numpy().view(np.int32)[0]))
+        # settled clocks, then the warm-up back to back with the timed steps
+        settle(cfg, layers, xs, ws, settle_ms)
         for i in range(10):
             moe.moe_forward_ep_partial(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], partial, lo, hi, ws)
         e0, e1 = HipEvent(), HipEvent()
-        torch.cuda.synchronize()
         e0.record(sh)
         for i in range(steps):
             moe.moe_forward_ep_partial(cfg, layers[i % len(layers)].weights, xs[i % len(xs)], partial, lo, hi, ws)
@@ -449,6 +451,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--settle-ms", type=float, default=40.0,
                     help="untimed steps before the first timed region, in host milliseconds")
+    ap.add_argument("--sweep-settle-ms", type=float, default=20.0,
+                    help="untimed steps before each later timed pass (after its setup's read-backs)")
     ap.add_argument("--workload", default=WORKLOAD,
                     help="configuration of the headline run (profiling other configurations)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -501,6 +505,7 @@ def main():
         for R in range(1, 9):
             xr = inputs(R)
             ur = union_sizes(cfg, layers, xr, ws)
+            settle(cfg, layers, xr, ws, args.sweep_settle_ms)
             r = timed_run(cfg, layers, xr, ur, base_shape.with_rows(R), R, args.sweep_steps, 10, ws)
             sweep.append(dict(rows=R, us_per_step=round(r["us_per_step"], 2), gbps=round(r["gbps"], 1),
                               frac=round(r["gbps"] / HBM_PEAK_GBPS, 4), mean_union=r["mean_union"]))
@@ -517,7 +522,9 @@ def main():
         for shp, R, kind in cases:
             xr = [torch.from_numpy(synth.activations(shp, s, rows=R).view(np.int16)).cuda() for s in range(N_INPUTS)]
             ur = union_sizes(cfg, layers, xr, ws)
+            settle(cfg, layers, xr, ws, args.sweep_settle_ms)
             a = timed_run(cfg, layers, xr, ur, shp, R, args.sweep_steps, 10, ws)
+            settle(cfg, layers, xr, ws, args.sweep_settle_ms)
             b = timed_run(cfg, layers, xr, ur, shp, R, args.sweep_steps, 10, ws, token_major=True)
             ab.append(dict(rows=R, rows_kind=kind, mean_union=a["mean_union"], pairs=R * shp.top_k,
                            union_us=round(a["us_per_step"], 2), token_major_us=round(b["us_per_step"], 2),
@@ -533,19 +540,22 @@ def main():
     wide = []
     if not args.no_sweep:
         c3 = synth.CONFIGS["c3_e256_verify4"]
-        wide.append(union_vs_subchunks(cfg, layers, c3.with_rows(12), 12, args.sweep_steps, ws))
+        wide.append(union_vs_subchunks(cfg, layers, c3.with_rows(12), 12, args.sweep_steps, ws,
+                                       args.sweep_settle_ms))
         log(f"[bench] rows>8: {wide[-1]}")
         c2 = synth.CONFIGS["c2_e128_verify2"]
         per_step = step_bytes(c2, 16, 16 * c2.top_k)["layer"]
         cfg2, layers2 = build_layers(c2, int(min(16, max(2, -(-(1 << 30) // per_step)))))
         ws2 = torch.zeros(moe.moe_workspace_bytes(cfg2), dtype=torch.uint8, device="cuda")
         for K in (12, 16):
-            wide.append(union_vs_subchunks(cfg2, layers2, c2.with_rows(K), K, args.sweep_steps, ws2))
+            wide.append(union_vs_subchunks(cfg2, layers2, c2.with_rows(K), K, args.sweep_steps, ws2,
+                                           args.sweep_settle_ms))
             log(f"[bench] rows>8: {wide[-1]}")
         del layers2, ws2
         torch.cuda.empty_cache()
 
-    configs = config_runs(args.sweep_steps, base_shape, layers, cfg, ws) if not args.no_sweep else []
+    configs = [] if args.no_sweep else config_runs(args.sweep_steps, base_shape, layers, cfg, ws,
+                                                   args.sweep_settle_ms)
 
     # One GPU's expert-parallel share at the real shape: the layer's 256
     # experts split over 8 GPUs, each sweeping its 32-expert range of the
@@ -554,7 +564,7 @@ def main():
     # part of the library and not timed).
     ep = None
     if not args.no_sweep:
-        ep = ep_shares(cfg, layers, xs, shape, args.rows, 8, args.sweep_steps, ws)
+        ep = ep_shares(cfg, layers, xs, shape, args.rows, 8, args.sweep_steps, ws, args.sweep_settle_ms)
         log(f"[bench] EP share rows={args.rows}, 8 ranges of {shape.num_experts // 8} experts: "
             f"local unions {[r['mean_local_union'] for r in ep['ranges']]}, "
             f"us {[r['us_per_step'] for r in ep['ranges']]}")
