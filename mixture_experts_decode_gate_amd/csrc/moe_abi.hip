@@ -50,8 +50,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Stage 2 is one kernel (down sweep and blend together) when every pair's
-// activations fit in LDS, else the down sweep and then the blend kernel.
+// Stage 2 is one kernel (down sweep and blend together) for one or two rows
+// whose pairs' activations all fit in LDS, else the down sweep and then the
+// blend kernel.
 const char* const kStageNames[] = {"route", "gate_up_sweep", "down_sweep_blend"};
 constexpr int kNumStages = 3;
 

@@ -88,8 +88,9 @@ hipError_t launch_union(const int32_t* ids, int rows, int k, int32_t* union_ids,
                         int32_t* slot_to_union, uint32_t* row_mask, hipStream_t s);
 hipError_t launch_gateup(const SweepParams& p, int rows, int max_slots, hipStream_t s, StageEvents ev = {});
 hipError_t launch_down(const SweepParams& p, hipStream_t s, StageEvents ev = {});
-// Down sweep and blend in one kernel for few rows: the rows of output each
-// block owns when this call can run it (every pair's act fits in LDS), else 0.
+// Down sweep and blend in one kernel for one or two rows: the rows of output
+// each block owns when this call can run it (at most two rows, every pair's
+// act fits in LDS), else 0.
 int down_blend_rows_per_block(int rows, int k, int h, int imax);
 hipError_t launch_down_blend(const SweepParams& p, int rows, int nr, hipStream_t s, StageEvents ev = {});
 // out = bf16(sum_j w*y + gamma*s); with partial non-null, partial = sum_j w*y
