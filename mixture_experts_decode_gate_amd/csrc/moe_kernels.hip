@@ -414,10 +414,13 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(SweepParams p) {
 // take over.
 constexpr int kDbThreads = 768;  // 12 waves, one block per CU
 constexpr int kDbMaxRows = 2;    // rows served by this kernel (act of every pair in LDS)
-constexpr int kDbActPer = 12;    // act staging loads per thread (16 bytes each)
+constexpr int kDbActPer = 12;    // act staging loads per thread (16 bytes each), at most
 
-template <int R, int NCH>
+// A: act staging loads per thread, enough for every pair of this call (the
+// loads are unconditional, so fewer of them when fewer pairs need staging).
+template <int R, int NCH, int A>
 __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, int nr) {
+  static_assert(A <= kDbActPer, "at most kDbActPer act staging loads per thread");
   static_assert(R <= kDbMaxRows, "down_blend_kernel serves at most kDbMaxRows rows");
   extern __shared__ u32x4 s_act[];  // [P][NCH][256] act rows (swizzled), then y as floats [P][nr]
   __shared__ SlotInfo s_slots[kNumSlots];
@@ -487,8 +490,8 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
   const float wv = ld_global(rp.w_out + tw);
   const int s2u = ld_global(rp.slot_to_union + tw);
   const float gv = ld_global(rp.gamma + ((int)threadIdx.x < R ? (int)threadIdx.x : 0));
-  u32x4 av_first[kDbActPer];
-  act_issue(av_first, 0, kDbActPer);
+  u32x4 av_first[A];
+  act_issue(av_first, 0, A);
   if (threadIdx.x == 0) {
     s_next = 0;
     s_slots[kSharedSlot] = shared_slot_info(rp, (1u << R) - 1u);
@@ -555,7 +558,7 @@ __global__ __launch_bounds__(kDbThreads) void down_blend_kernel(SweepParams p, i
     if ((int)threadIdx.x < R) s_gamma[threadIdx.x] = gv;
 #pragma unroll
     for (int q = 0; q < kTabPer; ++q) asm volatile("" ::"v"(tab[q]));
-    act_store(av_first, 0, kDbActPer);
+    act_store(av_first, 0, A);
   }
   __syncthreads();
   const int total = (s_union + 1) * nbat;
@@ -797,19 +800,29 @@ int max_lds_per_block() {
   return v;
 }
 
-template <int R>
-hipError_t down_blend_r(const SweepParams& p, int nr, hipStream_t s, StageEvents ev) {
+template <int R, int A>
+hipError_t down_blend_ra(const SweepParams& p, int nr, hipStream_t s, StageEvents ev) {
   const size_t lds = down_blend_dyn_lds(R, p.route.k, nr);
   static size_t attr_set[kMaxDevices] = {0};  // dynamic LDS limit set so far, per device
   const int dev = current_device();
   if (dev < 0 || dev >= kMaxDevices || attr_set[dev] < lds) {
-    const hipError_t e = hipFuncSetAttribute((const void*)down_blend_kernel<R, 1>,
+    const hipError_t e = hipFuncSetAttribute((const void*)down_blend_kernel<R, 1, A>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = lds;
   }
   const int grid = (p.h + nr - 1) / nr;
-  return launch_k(down_blend_kernel<R, 1>, dim3(grid), dim3(kDbThreads), lds, s, ev, p, nr);
+  return launch_k(down_blend_kernel<R, 1, A>, dim3(grid), dim3(kDbThreads), lds, s, ev, p, nr);
+}
+
+// 3 R staging loads per thread cover R (k + 1) pairs for k <= 8; larger k
+// takes kDbActPer.
+template <int R>
+hipError_t down_blend_r(const SweepParams& p, int nr, hipStream_t s, StageEvents ev) {
+  constexpr int kFew = 3 * R;
+  const int pairs = R * p.route.k + R;
+  if (pairs * kChunkUnits <= kFew * kDbThreads) return down_blend_ra<R, kFew>(p, nr, s, ev);
+  return down_blend_ra<R, kDbActPer>(p, nr, s, ev);
 }
 
 }  // namespace
@@ -873,7 +886,7 @@ int down_blend_rows_per_block(int rows, int k, int h, int imax) {
   const int per = (h + cu_count() - 1) / cu_count();
   const int nr = (per + kDownBatch - 1) / kDownBatch * kDownBatch;
   hipFuncAttributes fa;
-  if (hipFuncGetAttributes(&fa, (const void*)down_blend_kernel<kDbMaxRows, 1>) != hipSuccess) return 0;
+  if (hipFuncGetAttributes(&fa, (const void*)down_blend_kernel<kDbMaxRows, 1, kDbActPer>) != hipSuccess) return 0;
   if (fa.sharedSizeBytes + down_blend_dyn_lds(rows, k, nr) > (size_t)max_lds_per_block()) return 0;
   return nr;
 }

@@ -263,6 +263,12 @@ RAGGED = [
     synth.MoeShape("ids64", 1024, 96, 8, 128, 256, 8, synth.ROUTE_SIGMOID_BIAS, False, 1.5),
     synth.MoeShape("soft_nonorm", 4160, 40, 6, 2080, 64, 4, synth.ROUTE_SOFTMAX, False, 1.0),
     synth.MoeShape("k1", 128, 4, 1, 32, 32, 1, synth.ROUTE_SOFTMAX, True, 1.0),
+    # top_k past 8 at one and two rows: the fused down+blend kernel stages every pair's act in one pass up to
+    # 36 pairs (k = 35 at one row); k = 36 at one row takes the down sweep and the blend kernel instead
+    synth.MoeShape("k16_rows1", 512, 64, 16, 64, 96, 1, synth.ROUTE_SIGMOID_BIAS, True, 2.5),
+    synth.MoeShape("k12_rows2", 768, 48, 12, 96, 64, 2, synth.ROUTE_SOFTMAX, False, 1.0),
+    synth.MoeShape("k35_rows1", 256, 40, 35, 32, 32, 1, synth.ROUTE_SOFTMAX, True, 1.0),
+    synth.MoeShape("k36_rows1", 256, 40, 36, 32, 32, 1, synth.ROUTE_SIGMOID_BIAS, True, 2.5),
 ]
 
 
