@@ -91,17 +91,20 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     }
   };
   x_load(xv, 0, kXPass);
-  // Unconditional, with clamped indices: a branch around a load would leave
-  // the wait-count pass unsure of the count and make it wait for everything.
   // Wave w runs top-k for rows w, w + 8, ...; the prologue loads the inputs
   // of all of them, or with 16 keys per lane (past 256 experts) of the first
-  // only (the second row's are loaded when its turn comes).
+  // only (the second row's are loaded when its turn comes).  A wave with no
+  // row (w >= R) loads none: its redundant loads would sit in the in-order
+  // queue ahead of its first item's weights.  The branch is wave-uniform and
+  // every load after it is issued on both paths in the same order, so the
+  // waits below stay exact; the loads that do not depend on the wave
+  // (x, the pointer table) stay unconditional with clamped indices.
   constexpr int kTopkPre = G == 4 ? kTopkRows : 1;
-  TopkIn<G> tin[kTopkPre];
+  TopkIn<G> tin[kTopkPre] = {};
 #pragma unroll
   for (int i = 0; i < kTopkPre; ++i) {
     const int r = wave + i * kSweepWaves;
-    topk_load<G>(rp, r < R ? r : R - 1, lane, tin[i]);
+    if (r < R) topk_load<G>(rp, r, lane, tin[i]);
   }
   ExpertPtrs ep;
   if (kPtab) ep = expert_ptrs(rp, min((int)threadIdx.x, rp.E - 1));
