@@ -128,6 +128,76 @@ inline __device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows,
   return U;
 }
 
+// The same union over at most 256 experts through two LDS tables indexed by
+// expert id, in place of comparing every slot with every other: each slot t
+// whose id is in [lo, hi) takes the minimum of t into first[id] and sets its
+// row's bit in mask[id] (LDS atomics), and slot t is a first occurrence when
+// first[id] == t.  One wave's LDS operations run in issue order, so the reset
+// before the atomics and the reads after them need no barrier.  Writes what
+// union_wave writes, plus each first occurrence's slot table entry (built by
+// entry(id, row_mask) with no pairs) and then every slot's pair index into its
+// entry.  first and mask hold 256 entries; k <= 128 and n <= 128.
+template <typename EntryFn>
+inline __device__ int union_lds(const int32_t* ids_lds, int n, int k, int lo, int hi, int lane, uint32_t* first_tab,
+                                uint32_t* mask_tab, int32_t* union_ids, int32_t* union_count, int32_t* slot_to_union,
+                                uint32_t* row_mask, SlotInfo* slots, EntryFn&& entry) {
+  const int tiles = n > 64 ? 2 : 1;
+  // t / k for t < 128 and k <= 128 (checked for every pair)
+  const uint32_t kmagic = (65536u + (uint32_t)k - 1u) / (uint32_t)k;
+  int id[2], row[2];
+  bool use[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int t = 64 * q + lane;
+    id[q] = q < tiles && t < n ? ids_lds[t] : -1;
+    use[q] = q < tiles && t < n && id[q] >= lo && id[q] < hi;
+    row[q] = (int)(((uint32_t)t * kmagic) >> 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    if (use[q]) {
+      first_tab[id[q]] = 0xFFFFFFFFu;
+      mask_tab[id[q]] = 0u;
+    }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    if (use[q]) {
+      atomicMin(&first_tab[id[q]], (uint32_t)(64 * q + lane));
+      atomicOr(&mask_tab[id[q]], 1u << row[q]);
+    }
+  int f[2];
+  uint32_t msk[2];
+  bool first[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int t = 64 * q + lane;
+    f[q] = use[q] ? (int)first_tab[id[q]] : t;
+    msk[q] = use[q] ? mask_tab[id[q]] : 0u;
+    first[q] = use[q] && f[q] == t;
+  }
+  const uint64_t bal0 = __ballot(first[0]), bal1 = __ballot(first[1]);
+  const int U = __popcll(bal0) + __popcll(bal1);
+  auto pos_of = [&](int t) {
+    return t < 64 ? __popcll(bal0 & ((1ull << t) - 1ull)) : __popcll(bal0) + __popcll(bal1 & ((1ull << (t - 64)) - 1ull));
+  };
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int t = 64 * q + lane;
+    if (q < tiles && t < n) slot_to_union[t] = use[q] ? pos_of(f[q]) : -1;
+    if (first[q]) {
+      const int pos = pos_of(t);
+      union_ids[pos] = id[q];
+      row_mask[pos] = msk[q];
+      slots[pos] = entry(id[q], msk[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    if (use[q]) slots[pos_of(f[q])].pair[row[q]] = (uint8_t)(64 * q + lane);
+  if (lane == 0) *union_count = U;
+  return U;
+}
+
 // The token-major slot list (MoeLayer::forward_token_major_decode runs every
 // (row, selected expert) pair on its own): slot t = r*k + j holds id[t] for
 // row r alone, so an expert chosen by several rows is swept once per row.
@@ -406,6 +476,26 @@ __device__ __forceinline__ SlotInfo slot_info(const ExpertPtrs& e, int ex, int i
     const uint64_t m = slot_bits(eq, r * k, k);
     if (m) si.pair[r] = (uint8_t)(r * k + __builtin_ctzll(m));
   }
+  return si;
+}
+
+// A routed slot's table entry with no pair indices yet (all 0xFF).
+__device__ __forceinline__ SlotInfo slot_info_base(const ExpertPtrs& e, int ex, int inter, uint32_t row_mask) {
+  SlotInfo si;
+  si.gate_packed = e.p[0];
+  si.gate_scales = e.p[1];
+  si.up_packed = e.p[2];
+  si.up_scales = e.p[3];
+  si.down_packed = e.p[4];
+  si.down_scales = e.p[5];
+  si.gate_scale2 = e.scale2[0];
+  si.up_scale2 = e.scale2[1];
+  si.down_scale2 = e.scale2[2];
+  si.inter = inter;
+  si.row_mask = row_mask;
+  si.expert = ex;
+#pragma unroll
+  for (int r = 0; r < kMaxRows; ++r) si.pair[r] = (uint8_t)0xFF;
   return si;
 }
 

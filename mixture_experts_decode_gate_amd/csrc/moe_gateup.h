@@ -47,6 +47,7 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
   __shared__ float s_w[kMaxIds];
   __shared__ int32_t s_uids[kMaxIds], s_s2u[kMaxIds];
   __shared__ uint32_t s_rmask[kMaxIds];
+  __shared__ uint32_t s_first[G == 4 ? 256 : 1], s_umask[G == 4 ? 256 : 1];  // union_lds tables
   __shared__ int s_next;  // the block's next unclaimed item
   __shared__ int s_union;
   const int lane = threadIdx.x & 63;
@@ -208,16 +209,24 @@ __global__ __launch_bounds__(kMaxSweepThreads) void gateup_kernel(SweepParams p)
     UnionLane ul;
     // One row's top-k ids are distinct and already in first-occurrence order:
     // its union over the full expert range is the slot list itself.
-    if (p.token_major || (R == 1 && rp.expert_lo == 0 && rp.expert_hi >= rp.E))
-      identity_slots(s_ids, R * rp.k, rp.k, lane, s_uids, &s_union, s_s2u, s_rmask, ul);
-    else
-      union_wave(s_ids, R * rp.k, rp.k, R, rp.expert_lo, rp.expert_hi, lane, s_uids, &s_union, s_s2u, s_rmask, ul);
+    const bool identity = p.token_major || (R == 1 && rp.expert_lo == 0 && rp.expert_hi >= rp.E);
+    if (G == 4 && !identity) {
+      union_lds(s_ids, R * rp.k, rp.k, rp.expert_lo, rp.expert_hi, lane, s_first, s_umask, s_uids, &s_union, s_s2u,
+                s_rmask, s_slots, [&](int ex, uint32_t mask) {
+                  return slot_info_base(kPtab ? s_ptab[ex] : expert_ptrs(rp, ex), ex, rp.inter, mask);
+                });
+    } else {
+      if (identity)
+        identity_slots(s_ids, R * rp.k, rp.k, lane, s_uids, &s_union, s_s2u, s_rmask, ul);
+      else
+        union_wave(s_ids, R * rp.k, rp.k, R, rp.expert_lo, rp.expert_hi, lane, s_uids, &s_union, s_s2u, s_rmask, ul);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (ul.pos[q] >= 0) {  // slot 64*q + lane is the union entry's first slot
-        const int ex = s_ids[64 * q + lane];
-        s_slots[ul.pos[q]] = slot_info(kPtab ? s_ptab[ex] : expert_ptrs(rp, ex), ex, rp.inter, ul.mask[q], ul.eq[q],
-                                       rp.k, R);
+      for (int q = 0; q < 2; ++q) {
+        if (ul.pos[q] >= 0) {  // slot 64*q + lane is the union entry's first slot
+          const int ex = s_ids[64 * q + lane];
+          s_slots[ul.pos[q]] = slot_info(kPtab ? s_ptab[ex] : expert_ptrs(rp, ex), ex, rp.inter, ul.mask[q],
+                                         ul.eq[q], rp.k, R);
+        }
       }
     }
   }
