@@ -36,15 +36,24 @@ struct Slots128 {
   uint64_t lo, hi;
 };
 
-// Bits [a, a + k) of a slot set, k <= 64 (zero past slot 127).
-__device__ __forceinline__ uint64_t slot_bits(const Slots128& s, int a, int k) {
-  const uint64_t kmask = k >= 64 ? ~0ull : ((1ull << k) - 1ull);
-  uint64_t v;
-  if (a >= 128) v = 0ull;
-  else if (a >= 64) v = s.hi >> (a - 64);
-  else if (a == 0) v = s.lo;
-  else v = (s.lo >> a) | (s.hi << (64 - a));
-  return v & kmask;
+// Bits [lo, hi) of a 64-bit word, both bounds clamped to [0, 64].
+__device__ __forceinline__ uint64_t bit_range64(int lo, int hi) {
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > 64 ? 64 : hi;
+  if (hi <= lo) return 0ull;
+  const uint64_t up = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+  return up & ~((1ull << lo) - 1ull);
+}
+
+// The lowest slot of a slot set in [a, a + k) (a row's slots: a = r*k), or
+// -1 when none; a + k <= 128, so a row's window may span both words (one
+// row with top_k past 64).
+__device__ __forceinline__ int slot_first(const Slots128& s, int a, int k) {
+  const uint64_t lo = s.lo & bit_range64(a, a + k);
+  const uint64_t hi = s.hi & bit_range64(a - 64, a + k - 64);
+  if (lo) return __builtin_ctzll(lo);
+  if (hi) return 64 + __builtin_ctzll(hi);
+  return -1;
 }
 
 // One lane's part of the union: its slots t = 64*q + lane, q = 0, 1.
@@ -104,7 +113,7 @@ inline __device__ int union_wave(const int32_t* ids_lds, int n, int k, int rows,
     first[q] = t < n && local[q] && f[q] == t;
     ul.eq[q] = eq;
     for (int r = 0; r < rows; ++r)
-      if (slot_bits(eq, r * k, k)) ul.mask[q] |= 1u << r;
+      if (slot_first(eq, r * k, k) >= 0) ul.mask[q] |= 1u << r;
   }
   const uint64_t bal0 = __ballot(first[0]), bal1 = __ballot(first[1]);
   const int U = __popcll(bal0) + __popcll(bal1);
@@ -280,14 +289,15 @@ __device__ void topk_select(const RouteParams& p, int r, int lane, TopkIn<G>& in
   const int E = p.E, k = p.k;
   const bool softmax = p.route_kind == MOE_ROUTE_SOFTMAX;
   uint32_t key[G];  // 0: not a candidate (past E, or already taken)
-  int selj[G];      // round that took the expert, -1 if none
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const bool valid = lane * G + i < E;
     const float kf = softmax ? in.lv[i] : (float)in.sv[i] + in.bv[i];
     key[i] = valid ? key_bits(kf) : 0u;
-    selj[i] = -1;
   }
+  // Round j's id goes to lane j % 64 of sel[j / 64] (k <= 128); the ids are
+  // stored after the last round, so a round carries no store and no branch.
+  int sel[2] = {0, 0};
   float top_logit = 0.f;
   for (int j = 0; j < k; ++j) {
     uint32_t best = 0;
@@ -304,22 +314,35 @@ __device__ void topk_select(const RouteParams& p, int r, int lane, TopkIn<G>& in
     const int wi = __builtin_amdgcn_readlane(bi, wl);
     // k <= E valid keys keep m > 0; the clamp only guards ids against keys
     // outside the contract (NaN).
-    const int be = min(wl * G + wi, E - 1);
-    if (lane == wl) {
+    const int taken = wl * G + wi;
+    const int be = min(taken, E - 1);
 #pragma unroll
-      for (int i = 0; i < G; ++i)
-        if (i == wi) {
-          key[i] = 0u;
-          selj[i] = j;
-        }
-    }
+    for (int i = 0; i < G; ++i) key[i] = lane * G + i == taken ? 0u : key[i];
     if (j == 0) top_logit = key_float(m);  // softmax: the largest logit
-    if (lane == 0) {
-      if (ids_out != nullptr) ids_out[r * k + j] = be;
-      ids_lds[r * k + j] = be;
+    if (j < 64)
+      sel[0] = lane == j ? be : sel[0];
+    else
+      sel[1] = lane == j - 64 ? be : sel[1];
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int j = 64 * q + lane;
+    if (j < k) {
+      if (ids_out != nullptr) ids_out[r * k + j] = sel[q];
+      ids_lds[r * k + j] = sel[q];
     }
   }
   if (w_out == nullptr) return;
+  // round that took each of this lane's experts, -1 if none
+  int selj[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) selj[i] = -1;
+  for (int j = 0; j < k; ++j) {
+    const int e = __builtin_amdgcn_readlane(sel[j >> 6], j & 63);
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (lane * G + i == e) selj[i] = j;
+  }
   // Weights.  Softmax: exp(L - max), normalised over all experts, or over the
   // k selected when norm_topk_prob.  Sigmoid: s, optionally normalised over
   // the selected, times routed_scaling_factor.
@@ -473,8 +496,8 @@ __device__ __forceinline__ SlotInfo slot_info(const ExpertPtrs& e, int ex, int i
 #pragma unroll
   for (int r = 0; r < kMaxRows; ++r) si.pair[r] = (uint8_t)0xFF;
   for (int r = 0; r < rows; ++r) {
-    const uint64_t m = slot_bits(eq, r * k, k);
-    if (m) si.pair[r] = (uint8_t)(r * k + __builtin_ctzll(m));
+    const int f = slot_first(eq, r * k, k);
+    if (f >= 0) si.pair[r] = (uint8_t)f;
   }
   return si;
 }

@@ -269,6 +269,8 @@ RAGGED = [
     synth.MoeShape("k12_rows2", 768, 48, 12, 96, 64, 2, synth.ROUTE_SOFTMAX, False, 1.0),
     synth.MoeShape("k35_rows1", 256, 40, 35, 32, 32, 1, synth.ROUTE_SOFTMAX, True, 1.0),
     synth.MoeShape("k36_rows1", 256, 40, 36, 32, 32, 1, synth.ROUTE_SIGMOID_BIAS, True, 2.5),
+    # more than 64 selected experts: the two-tile union and the top-k's second id register
+    synth.MoeShape("k100_rows1", 256, 160, 100, 32, 32, 1, synth.ROUTE_SOFTMAX, True, 1.0),
 ]
 
 

@@ -168,6 +168,15 @@ def test_route_all_experts_and_norm_variants(kind, norm):
     check_route(rw, synth.activations(shape, 2))
 
 
+@pytest.mark.parametrize("E,k,rows", [(128, 65, 1), (200, 100, 1), (128, 128, 1), (256, 64, 2)])
+def test_route_more_than_64_selected(E, k, rows):
+    # top_k past one wave's lanes: the selected ids are held in two registers
+    # (lanes j and j - 64) until the last round; k = E selects every expert.
+    shape = synth.MoeShape(f"k{k}_e{E}", 512, E, k, 64, 64, rows, synth.ROUTE_SOFTMAX, True, 1.0)
+    rw = RouteWeights(shape)
+    check_route(rw, synth.activations(shape, 4))
+
+
 def test_route_zero_router_closed_form():
     shape = synth.MoeShape("zero", 256, 32, 4, 64, 64, 2, synth.ROUTE_SIGMOID_BIAS, True, 2.5)
     rw = RouteWeights(shape, router_w=np.zeros((32, 256), np.float32))
