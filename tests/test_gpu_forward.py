@@ -285,6 +285,28 @@ def test_ragged_and_edge_shapes(shape):
     assert np.array_equal(got, singles)
 
 
+TOP_K_PAST_64 = [
+    # one row whose slots span both 64-slot words: up to 256 experts (LDS-table union off the full range) and
+    # past 256 (16 top-k keys per lane, the pairwise-scan union); and k = 64 at two rows (row 1 fills the second)
+    (synth.MoeShape("k100_e160", 256, 160, 100, 32, 64, 1, synth.ROUTE_SOFTMAX, True, 1.0), [(0, 50), (50, 160)]),
+    (synth.MoeShape("k70_e300", 256, 300, 70, 32, 32, 1, synth.ROUTE_SIGMOID_BIAS, True, 2.5), [(0, 150), (150, 300)]),
+    (synth.MoeShape("k64_rows2", 256, 128, 64, 32, 32, 2, synth.ROUTE_SOFTMAX, False, 1.0), [(0, 64), (64, 128)]),
+]
+
+
+@pytest.mark.parametrize("shape,ranges", TOP_K_PAST_64, ids=[s.name for s, _ in TOP_K_PAST_64])
+def test_top_k_past_64_every_path(shape, ranges):
+    weights = synth.layer_weights(shape)
+    dl = upload(weights)
+    x = synth.activations(shape, 2)
+    check_against_oracle(weights, dl, x)
+    check_token_major(dl, x)
+    check_ep_shares(weights, dl, x, ranges)
+    if shape.rows > 1:
+        singles = np.stack([run_forward(dl, x[r:r + 1])[0][0] for r in range(shape.rows)])
+        assert np.array_equal(run_forward(dl, x)[0], singles)
+
+
 def test_graph_capture_replays():
     torch = torch_cuda()
     moe = moe_mod()
