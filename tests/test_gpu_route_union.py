@@ -248,6 +248,8 @@ def test_union_extremes():
     check_union(np.arange(128, dtype=np.int32).reshape(16, 8), 256)       # U = 128
     check_union(np.tile(np.arange(8, dtype=np.int32), (16, 1)), 256)       # 128 ids, U = 8
     check_union(np.arange(128, dtype=np.int32)[::-1].reshape(2, 64), 128)  # k = 64, two rows
+    check_union(np.arange(100, dtype=np.int32)[::-1].reshape(1, 100), 128)  # k = 100: one row's slots span both tiles
+    check_union(np.arange(128, dtype=np.int32).reshape(1, 128), 128)        # k = 128, one row
     # the second tile's first slot repeats the first tile's last id
     ids = np.arange(72, dtype=np.int32).reshape(9, 8)
     ids[8, 0] = 63
