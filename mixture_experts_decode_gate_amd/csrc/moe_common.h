@@ -36,8 +36,10 @@ struct Slots128 {
   uint64_t lo, hi;
 };
 
-// Bits [lo, hi) of a 64-bit word, both bounds clamped to [0, 64].
-__device__ __forceinline__ uint64_t bit_range64(int lo, int hi) {
+// Bits [lo, hi) of a 64-bit word, both bounds clamped to [0, 64].  This and
+// the other plain bit-arithmetic helpers below are host-callable too, so a
+// host program can check them against bit-by-bit references.
+__host__ __device__ __forceinline__ uint64_t bit_range64(int lo, int hi) {
   lo = lo < 0 ? 0 : lo;
   hi = hi > 64 ? 64 : hi;
   if (hi <= lo) return 0ull;
@@ -48,12 +50,23 @@ __device__ __forceinline__ uint64_t bit_range64(int lo, int hi) {
 // The lowest slot of a slot set in [a, a + k) (a row's slots: a = r*k), or
 // -1 when none; a + k <= 128, so a row's window may span both words (one
 // row with top_k past 64).
-__device__ __forceinline__ int slot_first(const Slots128& s, int a, int k) {
+__host__ __device__ __forceinline__ int slot_first(const Slots128& s, int a, int k) {
   const uint64_t lo = s.lo & bit_range64(a, a + k);
   const uint64_t hi = s.hi & bit_range64(a - 64, a + k - 64);
   if (lo) return __builtin_ctzll(lo);
   if (hi) return 64 + __builtin_ctzll(hi);
   return -1;
+}
+
+// t / k without a divide, for 0 <= t < 128 and 1 <= k <= 128.  With
+// m = ceil(2^16 / k) = (2^16 + e) / k, 0 <= e < k, t*m / 2^16 exceeds t/k by
+// t*e / (k * 2^16) < 1/k (t*e < 2^16); the fraction of t/k is at most
+// (k - 1)/k, so the sum stays below the next integer.
+__host__ __device__ __forceinline__ uint32_t small_div_magic(int k) {
+  return (65536u + (uint32_t)k - 1u) / (uint32_t)k;
+}
+__host__ __device__ __forceinline__ int small_div(int t, uint32_t magic) {
+  return (int)(((uint32_t)t * magic) >> 16);
 }
 
 // One lane's part of the union: its slots t = 64*q + lane, q = 0, 1.
@@ -151,8 +164,7 @@ inline __device__ int union_lds(const int32_t* ids_lds, int n, int k, int lo, in
                                 uint32_t* mask_tab, int32_t* union_ids, int32_t* union_count, int32_t* slot_to_union,
                                 uint32_t* row_mask, SlotInfo* slots, EntryFn&& entry) {
   const int tiles = n > 64 ? 2 : 1;
-  // t / k for t < 128 and k <= 128 (checked for every pair)
-  const uint32_t kmagic = (65536u + (uint32_t)k - 1u) / (uint32_t)k;
+  const uint32_t kmagic = small_div_magic(k);
   int id[2], row[2];
   bool use[2];
 #pragma unroll
@@ -160,7 +172,7 @@ inline __device__ int union_lds(const int32_t* ids_lds, int n, int k, int lo, in
     const int t = 64 * q + lane;
     id[q] = q < tiles && t < n ? ids_lds[t] : -1;
     use[q] = q < tiles && t < n && id[q] >= lo && id[q] < hi;
-    row[q] = (int)(((uint32_t)t * kmagic) >> 16);
+    row[q] = small_div(t, kmagic);
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q)
@@ -233,12 +245,12 @@ inline __device__ int identity_slots(const int32_t* ids_lds, int n, int k, int l
 
 // Order-preserving map of a float key to uint32 (larger float -> larger
 // integer); +0 and -0 map to neighbours, never to 0 except the all-ones NaN.
-__device__ __forceinline__ uint32_t key_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
+__host__ __device__ __forceinline__ uint32_t key_bits(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float key_float(uint32_t u) {
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+__host__ __device__ __forceinline__ float key_float(uint32_t u) {
+  return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
 // Weight pointers of one expert, staged in LDS by the block that runs top-k.
