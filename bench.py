@@ -48,13 +48,13 @@ sys.path.insert(0, ROOT)
 METRIC = "routed-MoE layer µs/step + achieved HBM GB/s (% peak), rows=1..8, NVFP4"
 
 # HBM traffic of the gate/up sweep at rows=8 per algorithmic byte, measured with
-# rocprofv3 --pmc over 121 dispatches (FETCH_SIZE x 2.000 + WRITE_SIZE; the factor comes
+# rocprofv3 --pmc over 119 dispatches (FETCH_SIZE x 2.000 + WRITE_SIZE; the factor comes
 # from a plain 1 GiB copy, see profiles/gateup_sweep_e256_rows1_2_4_8_pmc.md).  Valid only
 # for the kernel sources it was taken on; the roofline's traffic is this ratio times the
 # launch's algorithmic bytes.
 TRAFFIC_SOURCES = ('mixture_experts_decode_gate_amd/csrc/moe_gateup.h', 'mixture_experts_decode_gate_amd/csrc/moe_common.h',
                    'mixture_experts_decode_gate_amd/csrc/moe_device.h', 'mixture_experts_decode_gate_amd/csrc/moe_gateup_rows_5_8.hip')
-TRAFFIC_MEASURED = {"sources_sha256_16": "2814baa9c7881e49", "rows": 8, "gate_up_traffic_per_byte": 1.0023}
+TRAFFIC_MEASURED = {"sources_sha256_16": "93f46c421527a6ff", "rows": 8, "gate_up_traffic_per_byte": 1.0023}
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "c4_e256_prefill8"
 N_INPUTS = 16
